@@ -1,0 +1,261 @@
+"""fp64 CPU oracle of the fused ShortConv K/V step -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the bench's CPU-baseline leg may import this package.
+The HIP library never does, and this package imports nothing from it.
+
+The arithmetic lives in ``shortconv_oracle.c`` (fp64, one plain loop nest per definition step;
+its header states the definition and the readings of the pages it follows). This module only
+marshals numpy arrays into it and applies the two scatters the step ends with:
+
+* the cache write: row ``y[t]`` goes to ``cache[slot_mapping[t]]`` when ``0 <= slot < num_slots``
+  (aib.vote English news item on SGLang/Miles day-0 Inkling support, paragraph 2: the fused
+  kernel ends with the KV-cache write);
+* the state-pool write: the new window of sequence ``s`` goes to ``pool[state_idx[s]]`` when the
+  index is inside the pool (data-sketchers.com SGLang cookbook for Inkling-Small, section 2: the
+  sconv state lives in a per-request pool).
+
+Stored element types: ``"f32"`` arrays are ``numpy.float32``; ``"bf16"`` arrays are ``numpy.uint16``
+holding the bf16 bit patterns. Every pin of this oracle is in ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from contextlib import contextmanager
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+DTYPES = {"f32": (0, np.float32), "bf16": (1, np.uint16)}
+
+
+def _bind(lib):
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.sc_oracle_prefill.restype = ctypes.c_int
+    lib.sc_oracle_prefill.argtypes = [ctypes.c_int, I64, I64, I64, I64, P, P, I64, P, P,
+                                      ctypes.c_float, P, I64, P, P, P, P, P, ctypes.c_int]
+    lib.sc_oracle_decode.restype = ctypes.c_int
+    lib.sc_oracle_decode.argtypes = [ctypes.c_int, I64, I64, I64, I64, P, I64, P, P,
+                                     ctypes.c_float, P, I64, P, P, P, P, ctypes.c_int]
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _build
+            _build.build()
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+@contextmanager
+def library(path: str):
+    """Run the oracle from another build of its source (used by the tests that plant mistakes in
+    a copy of the oracle and check that the pins catch them)."""
+    global _lib
+    saved = _lib
+    _lib = _bind(ctypes.CDLL(path))
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+def _dtype_code(arr: np.ndarray) -> int:
+    for code, npdt in DTYPES.values():
+        if arr.dtype == npdt:
+            return code
+    raise TypeError(f"stored element type must be float32 or uint16 (bf16 bits), got {arr.dtype}")
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _token_rows(x: np.ndarray, H: int, D: int):
+    """Return (array, token stride in elements) for a [T, H, D] array whose inner two dims are
+    contiguous; the token dimension may be strided (e.g. a view into a wider projection)."""
+    if x.ndim != 3 or x.shape[1:] != (H, D):
+        raise ValueError(f"expected [T, {H}, {D}], got {x.shape}")
+    item = x.itemsize
+    if x.strides[2] != item or x.strides[1] != D * item or x.strides[0] % item:
+        x = np.ascontiguousarray(x)
+    stride = x.strides[0] // item if x.shape[0] > 0 else H * D
+    return x, max(stride, H * D)
+
+
+def prefill_one(x, cu_seqlens, taps, gamma, eps, state, state_idx, has_init, *, cond=False,
+                nthreads=1):
+    """One tensor (K or V) over packed sequences.
+
+    Returns ``(y, new_state, cond)``: y fp64 [T,H,D]; new_state stored [N,W-1,H,D] (None if W==1);
+    cond fp64 [T,H,D] or None. ``state_idx`` entries outside the pool mean "no state slot".
+    """
+    lib = _load()
+    taps = np.ascontiguousarray(taps, dtype=np.float32)
+    W, H, D = taps.shape
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    assert gamma.shape == (D,)
+    code = _dtype_code(x)
+    x, xs = _token_rows(x, H, D)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    N = cu.shape[0] - 1
+    T = x.shape[0]
+    assert N >= 0 and cu[0] == 0 and cu[-1] <= T and np.all(np.diff(cu) >= 0)
+    sidx = np.ascontiguousarray(state_idx if state_idx is not None else np.arange(N), dtype=np.int64)
+    hinit = np.ascontiguousarray(has_init if has_init is not None else np.ones(N), dtype=np.uint8)
+    if W > 1 and state is not None:
+        state = np.ascontiguousarray(state)
+        assert state.dtype == x.dtype and state.shape[1:] == (W - 1, H, D)
+        n_state = state.shape[0]
+    else:
+        state, n_state = None, 0
+    y = np.zeros((T, H, D), np.float64)
+    cnd = np.zeros((T, H, D), np.float64) if cond else None
+    new_state = np.zeros((N, W - 1, H, D), x.dtype) if W > 1 else None
+    rc = lib.sc_oracle_prefill(code, H, D, W, N, _ptr(cu), _ptr(x), xs, _ptr(taps), _ptr(gamma),
+                               float(eps), _ptr(state), n_state, _ptr(sidx), _ptr(hinit), _ptr(y),
+                               _ptr(cnd), _ptr(new_state), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle prefill rejected its arguments")
+    return y, new_state, cnd
+
+
+def decode_one(x_new, taps, gamma, eps, state, state_idx, *, cond=False, nthreads=1):
+    """One tensor (K or V), one new token per sequence. Returns ``(y, new_state, cond)`` as
+    ``prefill_one`` does; rows of new_state for an out-of-pool index are left zero."""
+    lib = _load()
+    taps = np.ascontiguousarray(taps, dtype=np.float32)
+    W, H, D = taps.shape
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    code = _dtype_code(x_new)
+    x_new, xs = _token_rows(x_new, H, D)
+    B = x_new.shape[0]
+    sidx = np.ascontiguousarray(state_idx if state_idx is not None else np.arange(B), dtype=np.int64)
+    if W > 1 and state is not None:
+        state = np.ascontiguousarray(state)
+        assert state.dtype == x_new.dtype and state.shape[1:] == (W - 1, H, D)
+        n_state = state.shape[0]
+    else:
+        state, n_state = None, 0
+    y = np.zeros((B, H, D), np.float64)
+    cnd = np.zeros((B, H, D), np.float64) if cond else None
+    new_state = np.zeros((B, W - 1, H, D), x_new.dtype) if W > 1 else None
+    rc = lib.sc_oracle_decode(code, H, D, W, B, _ptr(x_new), xs, _ptr(taps), _ptr(gamma),
+                              float(eps), _ptr(state), n_state, _ptr(sidx), _ptr(y), _ptr(cnd),
+                              _ptr(new_state), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle decode rejected its arguments")
+    return y, new_state, cnd
+
+
+@dataclass
+class StepResult:
+    """What one fused step produces, in the oracle's terms.
+
+    y_k, y_v:     fp64 [T,H,D] normalized rows in token order.
+    cond_k/v:     fp64 [T,H,D] rounding-error scale per element (or None).
+    slots:        int64 [T]: the cache row token t lands in, or -1 when it is not written.
+    k/v_state:    the whole state pool after the step (stored dtype), or None when W == 1.
+    """
+    y_k: np.ndarray
+    y_v: np.ndarray
+    cond_k: Optional[np.ndarray]
+    cond_v: Optional[np.ndarray]
+    slots: np.ndarray
+    k_state: Optional[np.ndarray]
+    v_state: Optional[np.ndarray]
+
+
+def cache_slots(slot_mapping, num_slots):
+    """Which cache row each token is written to; -1 where the slot is outside [0, num_slots)."""
+    sm = np.asarray(slot_mapping, dtype=np.int64)
+    return np.where((sm >= 0) & (sm < num_slots), sm, -1)
+
+
+def _scatter_state(pool, new_rows, state_idx):
+    if pool is None or new_rows is None:
+        return None
+    out = pool.copy()
+    idx = np.asarray(state_idx, dtype=np.int64)
+    ok = (idx >= 0) & (idx < pool.shape[0])
+    out[idx[ok]] = new_rows[ok]
+    return out
+
+
+def fused_prefill(k, v, cu_seqlens, k_taps, v_taps, k_gamma, v_gamma, eps, k_state, v_state,
+                  state_idx, has_initial_state, slot_mapping, num_slots, *, cond=True,
+                  nthreads=1) -> StepResult:
+    """The whole prefill step for K and V (same packing, state slots and cache slots)."""
+    N = len(cu_seqlens) - 1
+    sidx = np.arange(N) if state_idx is None else np.asarray(state_idx, np.int64)
+    yk, nk, ck = prefill_one(k, cu_seqlens, k_taps, k_gamma, eps, k_state, sidx,
+                             has_initial_state, cond=cond, nthreads=nthreads)
+    yv, nv, cv = prefill_one(v, cu_seqlens, v_taps, v_gamma, eps, v_state, sidx,
+                             has_initial_state, cond=cond, nthreads=nthreads)
+    return StepResult(yk, yv, ck, cv, cache_slots(slot_mapping, num_slots),
+                      _scatter_state(k_state, nk, sidx), _scatter_state(v_state, nv, sidx))
+
+
+def fused_decode(k_new, v_new, k_taps, v_taps, k_gamma, v_gamma, eps, k_state, v_state,
+                 state_idx, slot_mapping, num_slots, *, cond=True, nthreads=1) -> StepResult:
+    """The whole decode step for K and V."""
+    B = k_new.shape[0]
+    sidx = np.arange(B) if state_idx is None else np.asarray(state_idx, np.int64)
+    yk, nk, ck = decode_one(k_new, k_taps, k_gamma, eps, k_state, sidx, cond=cond,
+                            nthreads=nthreads)
+    yv, nv, cv = decode_one(v_new, v_taps, v_gamma, eps, v_state, sidx, cond=cond,
+                            nthreads=nthreads)
+    return StepResult(yk, yv, ck, cv, cache_slots(slot_mapping, num_slots),
+                      _scatter_state(k_state, nk, sidx), _scatter_state(v_state, nv, sidx))
+
+
+# ---------------------------------------------------------------------------------------------
+# The acceptance metric for floating-point outputs (used by the parity tests).
+#
+# A correct kernel that accumulates in fp32 cannot meet a pure element-wise relative bound on
+# elements whose taps cancel: the absolute error of a length-W dot product is a few units of
+# fp32 roundoff times sum_k |w_k e_k|, not times |c| (Higham, Accuracy and Stability of Numerical
+# Algorithms, 2nd ed., section 3.1). An element therefore passes when
+#     |g - y| <= tol * |y| + FLOOR_ULPS * 2^-24 * cond
+# with cond the oracle's error scale above, tol = 1e-5 for fp32 I/O and 3.9e-3 (one bf16 ulp in
+# relative terms, >= the round-to-nearest bound 2^-8/(1+2^-8)) for bf16 I/O.
+# ---------------------------------------------------------------------------------------------
+TOL = {"f32": 1e-5, "bf16": 3.9e-3}
+FLOOR_ULPS = 32.0
+
+
+def widen(arr: np.ndarray) -> np.ndarray:
+    """Exact widening of stored values (float32, or uint16 bf16 bits) to float64."""
+    if arr.dtype == np.uint16:
+        return (arr.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return arr.astype(np.float64)
+
+
+def compare(got: np.ndarray, y: np.ndarray, cond: np.ndarray, dtype: str):
+    """Element-wise acceptance test. ``got`` is stored values (float32 / uint16 bf16 bits).
+
+    Returns a dict: ok, worst (max error / bound), max_rel_well_conditioned (plain max relative
+    error over elements with cond <= 8|y|), n."""
+    g = widen(got)
+    err = np.abs(g - y)
+    bound = TOL[dtype] * np.abs(y) + FLOOR_ULPS * 2.0 ** -24 * cond
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, err / bound, np.where(err > 0, np.inf, 0.0))
+        well = cond <= 8.0 * np.abs(y)
+        rel = np.where(well & (y != 0), err / np.abs(y), 0.0)
+    finite = np.isfinite(g).all()
+    return {
+        "ok": bool(finite and (ratio <= 1.0).all()),
+        "worst": float(ratio.max()) if ratio.size else 0.0,
+        "max_rel_well_conditioned": float(rel.max()) if rel.size else 0.0,
+        "n": int(y.size),
+    }

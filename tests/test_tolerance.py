@@ -1,0 +1,103 @@
+"""The acceptance metric itself (CPU only).
+
+A numpy model of an fp32-accumulating kernel (products and sums rounded to fp32, one final
+rounding to the stored type) must pass the metric on realistic inputs, including heavy outliers,
+and results with a planted mistake must fail it. The model is test scaffolding for the metric,
+not a second oracle.
+"""
+import numpy as np
+
+import oracle
+import workloads
+
+
+def _fp32_model(x, cu, taps, gamma, eps, z, has_init, dtype):
+    f = np.float32
+    xw = oracle.widen(x).astype(f)
+    zw = oracle.widen(z).astype(f) if z is not None else None
+    W, H, D = taps.shape
+    R = W - 1
+    out = np.zeros(x.shape, f)
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        zz = zw[s] if (zw is not None and has_init[s]) else np.zeros((R, H, D), f)
+        e = np.concatenate([zz, xw[a:b]], axis=0)
+        c = taps[0] * e[0:b - a]
+        for k in range(1, W):
+            c = (c + taps[k] * e[k:k + b - a]).astype(f)
+        ss = np.zeros(c.shape[:2], f)
+        for d in range(D):
+            ss = (ss + c[:, :, d] * c[:, :, d]).astype(f)
+        r = np.sqrt((ss * f(1.0 / D) + f(eps)).astype(f)).astype(f)
+        inv = (f(1.0) / r).astype(f)
+        out[a:b] = (c * inv[:, :, None]).astype(f) * gamma
+    if dtype == "bf16":
+        return workloads.to_bf16_bits(out)
+    return out
+
+
+def _check(w, st, plant=None):
+    z = w.k_state[st.state_idx] if w.k_state is not None else None
+    g = _fp32_model(st.k, st.cu_seqlens, w.k_taps, w.k_gamma, w.eps, z, st.has_init, w.dtype)
+    if plant:
+        g = plant(g)
+    y, _, c = oracle.prefill_one(st.k, st.cu_seqlens, w.k_taps, w.k_gamma, w.eps, w.k_state,
+                                 st.state_idx, st.has_init, cond=True)
+    return oracle.compare(g, y, c, w.dtype)
+
+
+def test_fp32_model_passes_config1():
+    w = workloads.config(1)
+    r = _check(w, w.steps[0])
+    assert r["ok"], r
+    assert r["max_rel_well_conditioned"] <= oracle.TOL["f32"]
+
+
+def test_fp32_model_passes_bf16_with_outliers():
+    spec = workloads.Spec(dtype="bf16", H=8, D=128, W=8, seed=4, prefill_lens=[3000, 17],
+                          has_init=[0, 1], outlier_p=0.01, outlier_mul=50.0)
+    w = workloads.build(spec)
+    r = _check(w, w.steps[0])
+    assert r["ok"], r
+    assert r["max_rel_well_conditioned"] <= oracle.TOL["bf16"]
+
+
+def test_planted_errors_fail():
+    w = workloads.config(1)
+    st = w.steps[0]
+
+    def bump(g):
+        g = g.copy()
+        g[10, 0, 3] *= np.float32(1 + 5e-5)
+        return g
+
+    def swap(g):
+        g = g.copy()
+        g[[5, 6]] = g[[6, 5]]
+        return g
+
+    for plant in (bump, swap):
+        assert not _check(w, st, plant)["ok"], plant.__name__
+
+    spec = workloads.Spec(dtype="bf16", H=2, D=128, W=4, seed=8, prefill_lens=[200],
+                          has_init=[0])
+    wb = workloads.build(spec)
+
+    def two_ulps(g):
+        g = g.copy()
+        g[77, 1, 5] += np.uint16(2)
+        return g
+
+    assert _check(wb, wb.steps[0])["ok"]
+    assert not _check(wb, wb.steps[0], two_ulps)["ok"]
+
+
+def test_nonfinite_fails():
+    w = workloads.config(1)
+
+    def nan(g):
+        g = g.copy()
+        g[0, 0, 0] = np.nan
+        return g
+
+    assert not _check(w, w.steps[0], nan)["ok"]
