@@ -1,0 +1,348 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused ShortConv K/V step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload varlen_prefill] [--no-cpu-baseline]
+
+A step is one call of the fused step over one batch of the workload (for the default workload:
+8 packed sequences of U{512..4096} tokens, 8 KV heads x 128, W = 4, bf16 rows with fp32
+arithmetic, paged cache with 16-token blocks). Inputs are resident in HBM before timing starts.
+The batch is replicated into enough distinct device buffers that consecutive steps never find
+their data in the 256 MB Infinity Cache; step i uses replica i mod R.
+
+Prints ONE JSON line: tokens/s over the timed steps (wall clock between two device
+synchronizations), the average duration of the fused kernel from HIP events recorded around each
+launch on the launch stream, algorithmic HBM bytes / that duration against the 8 TB/s peak, the
+same for the decode step (256 sequences x 1 token), and the fp64 CPU oracle timed on host cores.
+
+Profiling helpers (run under rocprofv3, then summarize):
+    --calibrate-copy         also run a plain device copy of known size (counter calibration)
+    --summarize-profile DIR  turn rocprofv3 CSV output in DIR into a summary for profiles/
+"""
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused ShortConv K/V tokens/s + achieved HBM GB/s (% of 8 TB/s), prefill & decode"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
+MALL_BYTES = 256 << 20          # MI355X Infinity Cache
+KERNEL_SRC = os.path.join(ROOT, "causal_short_convolution_amd", "csrc", "kernels.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_varlen_bf16_traffic.md")
+WORKLOADS = {"tiny_ref": 1, "varlen_prefill": 2, "decode": 3, "long_prefill": 4, "mixed": 5}
+COPY_BYTES = 512 << 20          # calibration copy: 512 MiB read + 512 MiB written
+
+
+def kernel_source_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+# ------------------------------------------------------------------------------------------------
+# Algorithmic bytes: what the step must move, with no halo re-reads and no metadata caching.
+# R = H * D * element bytes (one token row of K or V).
+#   prefill: per token read K and V rows, write K and V cache rows, read the int64 slot (4R + 8);
+#            per sequence read cu_seqlens, state_idx, has_init (9 B) and write 2 (W-1) state rows,
+#            plus 2 (W-1) state rows read when it resumes from a stored state; taps and gamma once.
+#   decode:  per token 2R new rows + 2 (W-1) R state read + 2 (W-1) R state written + 2R cache
+#            rows + 8 B slot + 4 B state index; taps and gamma once.
+# ------------------------------------------------------------------------------------------------
+def algorithmic_bytes(w, step):
+    E = 4 if w.dtype == "f32" else 2
+    R = w.H * w.D * E
+    params = 2 * (w.W * w.H * w.D * 4 + w.D * 4)
+    if step.kind == "prefill":
+        T, N = step.tokens, step.num_seqs
+        n_init = int(step.has_init.sum()) if w.W > 1 else 0
+        state = 2 * (w.W - 1) * R * (N + n_init) if w.W > 1 else 0
+        return T * (4 * R + 8) + N * 9 + 4 + state + params
+    B = step.tokens
+    return B * (4 * R + 4 * (w.W - 1) * R + 12) + params
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="varlen_prefill", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU time budget of the oracle baseline sample")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize-profile", default=None, metavar="DIR")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------------------------------------
+# Device side
+# ------------------------------------------------------------------------------------------------
+def device_replicas(w, torch, n_rep, reseed=None):
+    """n_rep device copies of workload w's single step (fresh buffers each); for decode the slot
+    mappings differ between replicas (drawn with other seeds) so writes never revisit a row."""
+    import numpy as np
+    import workloads
+    from causal_short_convolution_amd import _binding  # noqa: F401  (fails loudly if not built)
+
+    dev = "cuda:0"
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def t(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(dt).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    shared = dict(k_taps=t(w.k_taps), v_taps=t(w.v_taps), k_gamma=t(w.k_gamma),
+                  v_gamma=t(w.v_gamma))
+    reps = []
+    st0 = w.steps[0]
+    for r in range(n_rep):
+        st = st0
+        num_slots = w.num_slots
+        if reseed is not None and r > 0:
+            w2 = reseed(r)
+            st, num_slots = w2.steps[0], w2.num_slots
+        d = dict(shared)
+        d["k"], d["v"] = t(st.k), t(st.v)
+        d["slot"] = t(st.slot_mapping.astype(np.int64))
+        d["sidx"] = t(st.state_idx.astype(np.int32))
+        if st.kind == "prefill":
+            d["cu"] = t(st.cu_seqlens.astype(np.int32))
+            d["hinit"] = t(st.has_init.astype(np.uint8))
+        d["k_state"], d["v_state"] = t(w.k_state), t(w.v_state)
+        d["num_slots"] = num_slots
+        reps.append(d)
+    # caches: prefill replicas each get their own; decode replicas share one pool large enough
+    # for every replica's slots (distinct random slots, so rows are not revisited)
+    if st0.kind == "prefill":
+        for d in reps:
+            d["k_cache"] = torch.empty((d["num_slots"], w.H, w.D), dtype=dt, device=dev)
+            d["v_cache"] = torch.empty((d["num_slots"], w.H, w.D), dtype=dt, device=dev)
+    else:
+        ns = max(d["num_slots"] for d in reps)
+        kc = torch.empty((ns, w.H, w.D), dtype=dt, device=dev)
+        vc = torch.empty((ns, w.H, w.D), dtype=dt, device=dev)
+        for d in reps:
+            d["k_cache"], d["v_cache"] = kc, vc
+    return reps
+
+
+def launcher(w, d):
+    from causal_short_convolution_amd import shortconv_kv_decode, shortconv_kv_prefill
+    if "cu" in d:
+        return lambda: shortconv_kv_prefill(
+            d["k"], d["v"], d["cu"], d["k_taps"], d["v_taps"], d["k_gamma"], d["v_gamma"], w.eps,
+            d["k_state"], d["v_state"], d["sidx"], d["hinit"], d["slot"], d["k_cache"],
+            d["v_cache"])
+    return lambda: shortconv_kv_decode(
+        d["k"], d["v"], d["k_taps"], d["v_taps"], d["k_gamma"], d["v_gamma"], w.eps, d["k_state"],
+        d["v_state"], d["sidx"], d["slot"], d["k_cache"], d["v_cache"])
+
+
+def time_steps(torch, fns, steps, warmup):
+    """Warm up, then time exactly `steps` launches: wall clock between two synchronizations, and
+    each launch's duration from a pair of events on the launch (current) stream."""
+    for i in range(warmup):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        fns[i % len(fns)]()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    return wall, kernel_ms
+
+
+def measure(torch, w, steps, warmup, reseed=None):
+    step = w.steps[0]
+    alg = algorithmic_bytes(w, step)
+    n_rep = max(2, math.ceil(2 * MALL_BYTES / alg) + 1)
+    reps = device_replicas(w, torch, n_rep, reseed)
+    fns = [launcher(w, d) for d in reps]
+    wall, kms = time_steps(torch, fns, steps, warmup)
+    kms_sorted = sorted(kms)
+    mean_ms = sum(kms) / len(kms)
+    return {
+        "tokens_per_step": step.tokens,
+        "replicas": n_rep,
+        "wall_s": wall,
+        "ms_per_step": 1e3 * wall / steps,
+        "tokens_per_s": step.tokens * steps / wall,
+        "kernel_us_mean": 1e3 * mean_ms,
+        "kernel_us_p10": 1e3 * kms_sorted[len(kms) // 10],
+        "kernel_us_p50": 1e3 * kms_sorted[len(kms) // 2],
+        "kernel_us_p90": 1e3 * kms_sorted[(9 * len(kms)) // 10],
+        "algorithmic_bytes": alg,
+        "achieved_GBps": alg / (mean_ms * 1e-3) / 1e9,
+    }
+
+
+def calibration_copy(torch):
+    n = COPY_BYTES // 2
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle, as it stands, on the same workload
+# ------------------------------------------------------------------------------------------------
+def cpu_baseline(w, budget_s):
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    st = w.steps[0]
+    reps = 0
+    c0, t0 = time.process_time(), time.perf_counter()
+    while True:
+        if st.kind == "prefill":
+            oracle.fused_prefill(st.k, st.v, st.cu_seqlens, w.k_taps, w.v_taps, w.k_gamma,
+                                 w.v_gamma, w.eps, w.k_state, w.v_state, st.state_idx,
+                                 st.has_init, st.slot_mapping, w.num_slots, cond=False,
+                                 nthreads=threads)
+        else:
+            oracle.fused_decode(st.k, st.v, w.k_taps, w.v_taps, w.k_gamma, w.v_gamma, w.eps,
+                                w.k_state, w.v_state, st.state_idx, st.slot_mapping, w.num_slots,
+                                cond=False, nthreads=threads)
+        reps += 1
+        if time.process_time() - c0 >= budget_s:
+            break
+    wall = time.perf_counter() - t0
+    return {"value": st.tokens * reps / wall, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole {w.name} workload ({st.tokens} tokens, K and V, fp64) "
+                      f"repeated {reps}x: {wall:.1f} s wall, "
+                      f"{time.process_time() - c0:.1f} s CPU on {threads} threads"}
+
+
+# ------------------------------------------------------------------------------------------------
+# Profile summaries (rocprofv3 CSV output -> a short text summary for profiles/)
+# ------------------------------------------------------------------------------------------------
+def summarize_profile(d):
+    import csv
+    out = []
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    for path in stats:
+        out.append(f"kernel stats: {os.path.relpath(path, d)}")
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                out.append(f"  {row.get('Name', '?')[:90]:90s} calls={row.get('Calls')} "
+                           f"avg_ns={float(row.get('AverageNs', 'nan')):.0f} "
+                           f"min_ns={row.get('MinNs')} max_ns={row.get('MaxNs')}")
+    ctrs = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    for path in ctrs:
+        agg = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                key = (row.get("Kernel_Name", "?"), row.get("Counter_Name", "?"))
+                agg.setdefault(key, []).append(float(row.get("Counter_Value", "nan")))
+        out.append(f"counters: {os.path.relpath(path, d)}")
+        for (k, c), vals in sorted(agg.items()):
+            out.append(f"  {k[:90]:90s} {c}: dispatch-rows={len(vals)} "
+                       f"mean={sum(vals) / len(vals):.1f}")
+    print("\n".join(out))
+
+
+# ------------------------------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the step shards with no communication across heads or sequences; see the design "
+              "notes)", file=sys.stderr)
+        return 2
+    from causal_short_convolution_amd import _binding
+    if not os.path.exists(_binding.LIBRARY_PATH):
+        from causal_short_convolution_amd import build
+        build.build()
+    import torch
+    import workloads
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+
+    n = WORKLOADS[args.workload]
+    w = workloads.config(n, seed=args.seed)
+    if len(w.steps) != 1:
+        raise SystemExit("bench.py: the mixed workload is measured by its two steps separately")
+    main_m = measure(torch, w, args.steps, args.warmup,
+                     reseed=(lambda r: workloads.config(n, seed=args.seed + 1000 * r))
+                     if w.steps[0].kind == "decode" else None)
+    extra = {}
+    if not args.no_decode and args.workload != "decode":
+        wd = workloads.config(3, seed=args.seed)
+        dm = measure(torch, wd, args.steps, args.warmup,
+                     reseed=lambda r: workloads.config(3, seed=args.seed + 1000 * r))
+        extra["decode"] = {"workload": "decode", "recipe": wd.recipe, **_round(dm),
+                           "frac_of_hbm_peak": dm["achieved_GBps"] / HBM_PEAK_GBPS}
+    if args.calibrate_copy:
+        calibration_copy(torch)
+
+    traffic = None
+    if os.path.exists(TRAFFIC_SUMMARY) and args.workload == "varlen_prefill":
+        txt = open(TRAFFIC_SUMMARY).read()
+        kv = dict(line.split(":", 1) for line in txt.splitlines() if line.startswith("- ")
+                  and ":" in line)
+        kv = {k[2:].strip(): v.strip() for k, v in kv.items()}
+        if kv.get("kernel_source_sha256") == kernel_source_sha():
+            traffic = float(kv["hbm_bytes_per_launch"])
+
+    st = w.steps[0]
+    line = {
+        "metric": METRIC,
+        "value": main_m["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "recipe": w.recipe, "seed": args.seed,
+                   "tokens_per_step": st.tokens, "seqs": st.num_seqs, "heads": w.H,
+                   "head_dim": w.D, "width": w.W, "io": w.dtype, "block_size": w.block_size,
+                   "replicas": main_m["replicas"], "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": main_m["achieved_GBps"], "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": main_m["achieved_GBps"] / HBM_PEAK_GBPS,
+                     "traffic": traffic,
+                     "kernel": "prefill_kernel" if st.kind == "prefill" else "decode_kernel",
+                     "algorithmic_bytes_per_launch": main_m["algorithmic_bytes"],
+                     "kernel_us_mean": main_m["kernel_us_mean"],
+                     "kernel_us_p50": main_m["kernel_us_p50"]},
+        **extra,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def _round(m):
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in m.items()}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,124 @@
+"""ctypes binding of libshortconv.so (argument marshalling only: every step runs in the library).
+
+Torch is used for device memory and streams: tensors are passed as raw device pointers and the
+current torch stream of their device is passed as the hipStream_t. The library must be built
+(``python -m causal_short_convolution_amd.build``); there is no fallback path of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_HERE, "libshortconv.so")
+
+SC_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+ERRORS = {-1: "SC_ERR_INVALID", -2: "SC_ERR_UNSUPPORTED", -3: "SC_ERR_HIP"}
+
+_lib = None
+
+
+class ShortConvError(RuntimeError):
+    """A non-zero return of the C ABI (message from shortconv_last_error)."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {message}")
+        self.code = code
+
+
+def load_library(path: str = LIBRARY_PATH):
+    """Load the built library (raises if it is missing: there is no other implementation)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built; run `python -m causal_short_convolution_amd.build` "
+            "(the fused ShortConv K/V step has no implementation other than this HIP library)")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.shortconv_kv_prefill.restype = ctypes.c_int
+    lib.shortconv_kv_prefill.argtypes = [P, P, I64, I64, P, I32, I64, P, P, P, P, F, P, P, I64, P,
+                                         P, P, P, P, I64, I32, I32, I32, I32, P]
+    lib.shortconv_kv_decode.restype = ctypes.c_int
+    lib.shortconv_kv_decode.argtypes = [P, P, I64, I64, I32, P, P, P, P, F, P, P, I64, P, P, P, P,
+                                        I64, I32, I32, I32, I32, P]
+    lib.shortconv_last_error.restype = ctypes.c_char_p
+    lib.shortconv_last_error.argtypes = []
+    lib.shortconv_abi_version.restype = ctypes.c_int
+    lib.shortconv_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load_library().shortconv_last_error().decode()
+
+
+def abi_version() -> int:
+    return int(load_library().shortconv_abi_version())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _rows(x: torch.Tensor, name: str):
+    """[tokens, H, D] with contiguous (H, D); returns the token stride in elements."""
+    if x.dim() != 3 or x.stride(2) != 1 or x.stride(1) != x.shape[2]:
+        raise ValueError(f"{name} must be [tokens, heads, head_dim] with contiguous heads/head_dim")
+    return x.stride(0) if x.shape[0] > 1 else x.shape[1] * x.shape[2]
+
+
+def _stream_handle(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise ShortConvError(rc, last_error())
+
+
+def shortconv_kv_prefill(k, v, cu_seqlens, k_taps, v_taps, k_gamma, v_gamma, eps, k_state, v_state,
+                         state_idx, has_initial_state, slot_mapping, k_cache, v_cache, *,
+                         stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Fused ShortConv K/V prefill over packed sequences (see include/shortconv.h).
+
+    k, v [T,H,D] (fp32 or bf16); cu_seqlens int32 [N+1]; taps fp32 [W,H,D]; gamma fp32 [D];
+    k_state/v_state [S,W-1,H,D] or None (W == 1); state_idx int32 [N] or None;
+    has_initial_state uint8/bool [N] or None; slot_mapping int64 [T]; caches [num_slots,H,D].
+    """
+    lib = load_library()
+    W, H, D = k_taps.shape
+    if has_initial_state is not None and has_initial_state.dtype == torch.bool:
+        has_initial_state = has_initial_state.view(torch.uint8)
+    S = k_state.shape[0] if k_state is not None else 0
+    with torch.cuda.device(k.device):
+        rc = lib.shortconv_kv_prefill(
+            _ptr(k), _ptr(v), _rows(k, "k"), _rows(v, "v"), _ptr(cu_seqlens),
+            cu_seqlens.shape[0] - 1, k.shape[0], _ptr(k_taps), _ptr(v_taps), _ptr(k_gamma),
+            _ptr(v_gamma), float(eps), _ptr(k_state), _ptr(v_state), S, _ptr(state_idx),
+            _ptr(has_initial_state), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache),
+            k_cache.shape[0], H, D, W, SC_DTYPE[k.dtype], _stream_handle(k.device, stream))
+    _check(rc)
+
+
+def shortconv_kv_decode(k_new, v_new, k_taps, v_taps, k_gamma, v_gamma, eps, k_state, v_state,
+                        state_idx, slot_mapping, k_cache, v_cache, *,
+                        stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Fused ShortConv K/V decode, one new token per sequence (see include/shortconv.h)."""
+    lib = load_library()
+    W, H, D = k_taps.shape
+    S = k_state.shape[0] if k_state is not None else 0
+    with torch.cuda.device(k_new.device):
+        rc = lib.shortconv_kv_decode(
+            _ptr(k_new), _ptr(v_new), _rows(k_new, "k_new"), _rows(v_new, "v_new"),
+            k_new.shape[0], _ptr(k_taps), _ptr(v_taps), _ptr(k_gamma), _ptr(v_gamma), float(eps),
+            _ptr(k_state), _ptr(v_state), S, _ptr(state_idx), _ptr(slot_mapping), _ptr(k_cache),
+            _ptr(v_cache), k_cache.shape[0], H, D, W, SC_DTYPE[k_new.dtype],
+            _stream_handle(k_new.device, stream))
+    _check(rc)

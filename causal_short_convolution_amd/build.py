@@ -1,0 +1,46 @@
+"""Build libshortconv.so (the C-ABI library with the gfx950 kernels) in-tree with hipcc.
+
+    python -m causal_short_convolution_amd.build [--save-temps DIR]
+
+Flags: gfx950 only; -ffp-contract=off so the kernels' fused multiply-adds are exactly the
+explicit ones; packed-fp32 instruction selection disabled; hidden visibility so the library
+exports only the extern "C" entry points declared in include/shortconv.h.
+"""
+import argparse
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libshortconv.so")
+SOURCES = [os.path.join(CSRC, f) for f in ("kernels.hip", "abi.hip")]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
+    "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def build(verbose: bool = False, save_temps: str = None) -> str:
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, *SOURCES]
+    cwd = None
+    if save_temps:
+        os.makedirs(save_temps, exist_ok=True)
+        cmd.insert(1, "--save-temps")
+        cwd = save_temps
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True, cwd=cwd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--save-temps", default=None, help="keep intermediate files (ISA) in DIR")
+    args = ap.parse_args()
+    print(build(verbose=True, save_temps=args.save_temps))

@@ -1,0 +1,163 @@
+// C ABI of the fused ShortConv K/V step: host-side validation, problem geometry and launch.
+// The operation, layouts and error behaviour are specified in include/shortconv.h.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "shortconv.h"
+#include "shortconv_internal.h"
+
+#define SC_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int element_bytes(int32_t dtype) { return dtype == SC_DTYPE_F32 ? 4 : 2; }
+
+// Checks shared by both entry points. Returns SC_OK or an error (message set).
+int check_common(const char* fn, const void* x0, const void* x1, int64_t s0, int64_t s1,
+                 const float* t0, const float* t1, const float* g0, const float* g1, float eps,
+                 const void* st0, const void* st1, int64_t num_state_slots, const int64_t* slot,
+                 const void* c0, const void* c1, int64_t num_slots, int32_t heads, int32_t D,
+                 int32_t W, int32_t dtype, int64_t tokens) {
+    if (dtype != SC_DTYPE_F32 && dtype != SC_DTYPE_BF16)
+        return fail(SC_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+    if (D != 64 && D != 128 && D != 256)
+        return fail(SC_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128, 256}", fn, D);
+    if (W < 1 || W > 8) return fail(SC_ERR_UNSUPPORTED, "%s: width %d not in [1, 8]", fn, W);
+    if (heads < 1) return fail(SC_ERR_INVALID, "%s: num_heads %d < 1", fn, heads);
+    // Arrays with no elements may be null (an empty tensor's data pointer can be).
+    if (tokens > 0 && (!x0 || !x1)) return fail(SC_ERR_INVALID, "%s: null K or V input", fn);
+    if (tokens > 0 && !slot) return fail(SC_ERR_INVALID, "%s: null slot_mapping", fn);
+    if (!t0 || !t1 || !g0 || !g1) return fail(SC_ERR_INVALID, "%s: null taps or gamma", fn);
+    if (num_slots > 0 && (!c0 || !c1)) return fail(SC_ERR_INVALID, "%s: null K or V cache", fn);
+    if (W > 1 && num_state_slots > 0 && (!st0 || !st1))
+        return fail(SC_ERR_INVALID, "%s: null conv state with width %d > 1", fn, W);
+    if (num_slots < 0) return fail(SC_ERR_INVALID, "%s: num_slots < 0", fn);
+    if (num_state_slots < 0) return fail(SC_ERR_INVALID, "%s: num_state_slots < 0", fn);
+    if (!(eps >= 0.0f) || eps > 3.0e38f)
+        return fail(SC_ERR_INVALID, "%s: eps must be finite and >= 0", fn);
+    const int64_t row = (int64_t)heads * D;
+    if (row > (int64_t)1 << 20) return fail(SC_ERR_UNSUPPORTED, "%s: num_heads too large", fn);
+    const int eb = element_bytes(dtype);
+    if (s0 < row || s1 < row)
+        return fail(SC_ERR_INVALID, "%s: token stride smaller than num_heads*head_dim", fn);
+    if ((s0 * eb) % 16 || (s1 * eb) % 16)
+        return fail(SC_ERR_INVALID, "%s: token stride must be a multiple of 16 bytes", fn);
+    const void* ptrs[] = {x0, x1, t0, t1, g0, g1, c0, c1, st0, st1};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(SC_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
+    return SC_OK;
+}
+
+sc::StepArgs make_args(const void* k, const void* v, int64_t ks, int64_t vs, const float* kt,
+                       const float* vt, const float* kg, const float* vg, float eps, void* kst,
+                       void* vst, int64_t num_state_slots, const int32_t* state_idx,
+                       const int64_t* slot, void* kc, void* vc, int64_t num_slots, int32_t heads,
+                       int32_t D, int32_t W, int32_t dtype) {
+    sc::StepArgs a = {};
+    a.x[0] = k;
+    a.x[1] = v;
+    a.x_stride[0] = ks;
+    a.x_stride[1] = vs;
+    a.taps[0] = kt;
+    a.taps[1] = vt;
+    a.gamma[0] = kg;
+    a.gamma[1] = vg;
+    a.state[0] = W > 1 ? kst : nullptr;
+    a.state[1] = W > 1 ? vst : nullptr;
+    a.cache[0] = kc;
+    a.cache[1] = vc;
+    a.state_idx = state_idx;
+    a.slot = slot;
+    a.num_slots = num_slots;
+    a.num_state_slots = W > 1 ? num_state_slots : 0;
+    a.heads = heads;
+    const int vec = 16 / element_bytes(dtype);
+    a.lanes_per_tensor = heads * (D / vec);
+    a.lane_blocks = (int32_t)((2 * (int64_t)a.lanes_per_tensor + 255) / 256);
+    a.eps = eps;
+    return a;
+}
+
+}  // namespace
+
+SC_API int shortconv_kv_prefill(const void* k, const void* v, int64_t k_tok_stride,
+                                int64_t v_tok_stride, const int32_t* cu_seqlens, int32_t num_seqs,
+                                int64_t total_tokens, const float* k_taps, const float* v_taps,
+                                const float* k_gamma, const float* v_gamma, float eps,
+                                void* k_state, void* v_state, int64_t num_state_slots,
+                                const int32_t* state_idx, const uint8_t* has_initial_state,
+                                const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                int64_t num_slots, int32_t num_heads, int32_t head_dim,
+                                int32_t width, int32_t dtype, void* stream) {
+    const char* fn = "shortconv_kv_prefill";
+    g_err[0] = 0;
+    int rc = check_common(fn, k, v, k_tok_stride, v_tok_stride, k_taps, v_taps, k_gamma, v_gamma,
+                          eps, k_state, v_state, num_state_slots, slot_mapping, k_cache, v_cache,
+                          num_slots, num_heads, head_dim, width, dtype, total_tokens);
+    if (rc != SC_OK) return rc;
+    if (num_seqs < 0) return fail(SC_ERR_INVALID, "%s: num_seqs < 0", fn);
+    if (total_tokens < 0 || total_tokens > INT32_MAX)
+        return fail(SC_ERR_INVALID, "%s: total_tokens must be in [0, 2^31)", fn);
+    if (num_seqs == 0) return SC_OK;  // no sequence owns any token: nothing to do
+    if (!cu_seqlens) return fail(SC_ERR_INVALID, "%s: null cu_seqlens", fn);
+    if (width == 1 && total_tokens == 0) return SC_OK;
+
+    sc::StepArgs a = make_args(k, v, k_tok_stride, v_tok_stride, k_taps, v_taps, k_gamma, v_gamma,
+                               eps, k_state, v_state, num_state_slots, state_idx, slot_mapping,
+                               k_cache, v_cache, num_slots, num_heads, head_dim, width, dtype);
+    a.cu = cu_seqlens;
+    a.has_init = has_initial_state;
+    a.tokens = total_tokens;
+    a.num_seqs = num_seqs;
+    const int bt = sc::prefill_tile_tokens(dtype, head_dim, width);
+    const int64_t tiles = total_tokens / bt + num_seqs;
+    if (tiles * a.lane_blocks + 8 > INT32_MAX)
+        return fail(SC_ERR_UNSUPPORTED, "%s: problem too large for one launch", fn);
+    a.tiles = (int32_t)tiles;
+    hipError_t e = sc::launch_prefill(a, dtype, head_dim, width, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(SC_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return SC_OK;
+}
+
+SC_API int shortconv_kv_decode(const void* k_new, const void* v_new, int64_t k_tok_stride,
+                               int64_t v_tok_stride, int32_t batch, const float* k_taps,
+                               const float* v_taps, const float* k_gamma, const float* v_gamma,
+                               float eps, void* k_state, void* v_state, int64_t num_state_slots,
+                               const int32_t* state_idx, const int64_t* slot_mapping,
+                               void* k_cache, void* v_cache, int64_t num_slots,
+                               int32_t num_heads, int32_t head_dim, int32_t width, int32_t dtype,
+                               void* stream) {
+    const char* fn = "shortconv_kv_decode";
+    g_err[0] = 0;
+    int rc = check_common(fn, k_new, v_new, k_tok_stride, v_tok_stride, k_taps, v_taps, k_gamma,
+                          v_gamma, eps, k_state, v_state, num_state_slots, slot_mapping, k_cache,
+                          v_cache, num_slots, num_heads, head_dim, width, dtype, batch);
+    if (rc != SC_OK) return rc;
+    if (batch < 0) return fail(SC_ERR_INVALID, "%s: batch < 0", fn);
+    if (batch == 0) return SC_OK;
+    sc::StepArgs a = make_args(k_new, v_new, k_tok_stride, v_tok_stride, k_taps, v_taps, k_gamma,
+                               v_gamma, eps, k_state, v_state, num_state_slots, state_idx,
+                               slot_mapping, k_cache, v_cache, num_slots, num_heads, head_dim,
+                               width, dtype);
+    a.tokens = batch;
+    if (a.lane_blocks > 65535) return fail(SC_ERR_UNSUPPORTED, "%s: num_heads too large", fn);
+    hipError_t e = sc::launch_decode(a, dtype, head_dim, width, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(SC_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return SC_OK;
+}
+
+SC_API const char* shortconv_last_error(void) { return g_err; }
+
+SC_API int shortconv_abi_version(void) { return SHORTCONV_ABI_VERSION; }

@@ -1,0 +1,434 @@
+// HIP kernels of the fused ShortConv K/V step for gfx950 (MI355X).
+//
+// The step is a memory-bound stencil over tokens (causal depthwise convolution of width W over the
+// projected K and V, aib.vote English news item on SGLang/Miles Inkling support, paragraphs 1-2;
+// the window is the current row and the W-1 before it, axbrief.com Inkling specifications blog,
+// SConv section), followed by RMSNorm over head_dim, the paged KV-cache write and the
+// conv-state update. It has ~(2W+4) flops per element against 2 bytes read and 2 written in bf16,
+// far under the fp32 vector ridge of the chip, so no matrix cores are involved: the design is
+// about moving each byte once with full-width memory instructions.
+//
+// Thread layout (prefill and decode alike): one lane owns 16 bytes of one token row of one tensor,
+// i.e. VEC = 8 bf16 or 4 fp32 channels of one head. LPH = D / VEC lanes cover a head; a 64-wide
+// wavefront covers 64 * 16 B = 1 KiB of a row, so every global load and store is a fully used,
+// contiguous 16-byte-per-lane access. Lanes [0, lanes_per_tensor) work on K and the rest on V.
+//
+// Prefill tiles: a workgroup walks BT consecutive tokens of ONE sequence, keeping the sliding
+// window in registers (each input row is loaded once and reused by the W outputs that read it).
+// A tile's W-1 row halo is the tail of the previous tile of the same sequence, or the sequence's
+// conv state / zeros for its first tile. Tiles never straddle sequences: sequence s owns logical
+// tiles [P(s), P(s) + max(1, ceil(L_s / BT))) with P(s) = floor(cu[s] / BT) + s. P is strictly
+// increasing and P(s) + max(1, ceil(L_s/BT)) <= P(s+1), so a workgroup finds its sequence by binary
+// search over cu_seqlens with no host-side scan; at most one logical tile per sequence is empty.
+//
+// Conv-state ownership: only the first tile of a sequence reads the old state (its halo), so that
+// tile also writes the new state (the sequence's last W-1 raw rows, taken from the read-only input
+// and, when the sequence is shorter than W-1, from the surviving old rows). No other workgroup
+// touches that state row, so no grid-wide synchronization is needed.
+//
+// XCD-aware order: the chip hands consecutive workgroup ids to its 8 XCDs in turn, and each XCD
+// has its own L2. Logical tiles are remapped so that every XCD processes one contiguous run of
+// tiles; a tile's halo rows were then just loaded by its neighbour on the same XCD and are served
+// from that L2 instead of HBM.
+//
+// Numerics (shared by prefill and decode through fused_row, so the two are bit-identical):
+// inputs widen exactly to fp32; c = taps[0]*x[0], then fma over k = 1..W-1; the sum of squares is an
+// fma chain over the lane's channels followed by an xor-butterfly across the LPH lanes (every lane
+// ends with the same bits, since each step adds the same two values); r = sqrt(ss/D + eps) and 1/r
+// are correctly rounded; y = (c * (1/r)) * gamma, rounded once to the element type (round to
+// nearest even). With eps = 0, scaling the inputs by a power of two leaves y bit-identical.
+#include "shortconv_internal.h"
+
+namespace sc {
+namespace {
+
+constexpr int kBlock = 256;  // threads per workgroup (4 wavefronts)
+constexpr int kXcds = 8;
+
+// ------------------------------------------------------------------------------------------------
+// Element types. A "packet" is the 16 bytes one lane moves: uint4.
+// ------------------------------------------------------------------------------------------------
+struct F32 {
+    static constexpr int VEC = 4;
+    static constexpr int BYTES = 4;
+    __device__ static inline void widen(const uint4& r, float (&f)[VEC]) {
+        f[0] = __uint_as_float(r.x);
+        f[1] = __uint_as_float(r.y);
+        f[2] = __uint_as_float(r.z);
+        f[3] = __uint_as_float(r.w);
+    }
+    __device__ static inline uint4 narrow(const float (&f)[VEC]) {
+        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                          __float_as_uint(f[3]));
+    }
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+struct BF16 {
+    static constexpr int VEC = 8;
+    static constexpr int BYTES = 2;
+    __device__ static inline void widen(const uint4& r, float (&f)[VEC]) {
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[2 * i] = __uint_as_float(w[i] << 16);
+            f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    // Round to nearest even (one v_cvt_pk_bf16_f32 per pair on gfx950).
+    __device__ static inline uint32_t pack2(float a, float b) {
+        bf16x2_t p = {(__bf16)a, (__bf16)b};
+        return __builtin_bit_cast(uint32_t, p);
+    }
+    __device__ static inline uint4 narrow(const float (&f)[VEC]) {
+        return make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]),
+                          pack2(f[6], f[7]));
+    }
+};
+
+__device__ inline uint4 ld16(const void* base, int64_t elem_off, int bytes) {
+    return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) + elem_off * bytes);
+}
+__device__ inline void st16(void* base, int64_t elem_off, int bytes, const uint4& v) {
+    *reinterpret_cast<uint4*>(static_cast<char*>(base) + elem_off * bytes) = v;
+}
+// Row access as (wave-uniform byte base, per-lane 32-bit byte offset).
+__device__ inline uint4 ldrow(const char* base, uint32_t lane_off) {
+    return *reinterpret_cast<const uint4*>(base + lane_off);
+}
+__device__ inline void strow(char* base, uint32_t lane_off, const uint4& v) {
+    *reinterpret_cast<uint4*>(base + lane_off) = v;
+}
+
+// Values that are the same in every lane, moved to scalar registers so that the compiler uses
+// scalar loads for per-token metadata and scalar base addresses for the row accesses.
+__device__ inline int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline int64_t uniform(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Data-parallel-primitive lane moves (row = 16 lanes).
+template <int CTRL>
+__device__ inline float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141; // lane i <-> 7-i within each half row
+constexpr int kRowMirror = 0x140;     // lane i <-> 15-i within each row
+
+// Sum over the LPH lanes that own one head (aligned groups, LPH | 64). A butterfly: at every step
+// each lane adds its value and its partner's, the partner adds the same two values in the other
+// order, so all lanes of the group end with the same bits. Within a 16-lane row the partners come
+// from DPP moves; the quad steps make the 4 lanes of a quad equal, so the mirror moves pair each
+// lane with a lane of the neighbouring quad (half row) or half row (row).
+template <int LPH>
+__device__ inline float head_sum(float v) {
+    static_assert(LPH == 8 || LPH == 16 || LPH == 32 || LPH == 64, "lanes per head");
+    v += dpp<kQuadXor1>(v);
+    v += dpp<kQuadXor2>(v);
+    v += dpp<kRowHalfMirror>(v);
+    if (LPH >= 16) v += dpp<kRowMirror>(v);
+    if (LPH >= 32) v += __shfl_xor(v, 16, 64);
+    if (LPH >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// Per-lane constants of one (tensor, head, 16-byte column) position.
+template <class E, int W>
+struct LaneParams {
+    float tap[W][E::VEC];
+    float gam[E::VEC];
+};
+
+template <class E, int W>
+__device__ inline void load_params(const float* taps, const float* gamma, int heads, int D, int h,
+                                   int d0, LaneParams<E, W>& p) {
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        const float* t = taps + ((int64_t)k * heads + h) * D + d0;
+#pragma unroll
+        for (int v = 0; v < E::VEC; v += 4) {
+            const float4 q = *reinterpret_cast<const float4*>(t + v);
+            p.tap[k][v] = q.x;
+            p.tap[k][v + 1] = q.y;
+            p.tap[k][v + 2] = q.z;
+            p.tap[k][v + 3] = q.w;
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < E::VEC; v += 4) {
+        const float4 q = *reinterpret_cast<const float4*>(gamma + d0 + v);
+        p.gam[v] = q.x;
+        p.gam[v + 1] = q.y;
+        p.gam[v + 2] = q.z;
+        p.gam[v + 3] = q.w;
+    }
+}
+
+// The row math of one output row slice: window win[0..W-1] (win[W-1] = current token).
+template <class E, int W, int LPH>
+__device__ inline uint4 fused_row(const float (&win)[W][E::VEC], const LaneParams<E, W>& p,
+                                  float eps, float inv_d) {
+    constexpr int VEC = E::VEC;
+    float c[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) c[v] = p.tap[0][v] * win[0][v];
+#pragma unroll
+    for (int k = 1; k < W; ++k)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) c[v] = __builtin_fmaf(p.tap[k][v], win[k][v], c[v]);
+    float ss = 0.0f;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) ss = __builtin_fmaf(c[v], c[v], ss);
+    ss = head_sum<LPH>(ss);
+    const float r = __builtin_sqrtf(__builtin_fmaf(ss, inv_d, eps));
+    const float inv = 1.0f / r;
+    float o[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) o[v] = (c[v] * inv) * p.gam[v];
+    return E::narrow(o);
+}
+
+__device__ inline int32_t clamp_tok(int32_t v, int64_t T) {
+    return v < 0 ? 0 : (v > T ? (int32_t)T : v);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Prefill
+// ------------------------------------------------------------------------------------------------
+template <int BT>
+__device__ inline int64_t tile_base(const int32_t* cu, int s, int64_t T) {
+    return (int64_t)(clamp_tok(cu[s], T) / BT) + s;
+}
+
+// Process n (<= BT) tokens starting at t0 with the window rows win[0..W-2] already in place.
+// xb: byte address of token t0's row (wave-uniform); lane_off: this lane's byte offset in a row.
+template <class E, int D, int W, int BT, bool FULL>
+__device__ inline void prefill_tokens(const StepArgs& a, const LaneParams<E, W>& p,
+                                      float (&win)[W][E::VEC], const char* xb,
+                                      int64_t stride_bytes, char* cache, int64_t row_bytes,
+                                      uint32_t lane_off, int64_t t0, int n) {
+    constexpr int LPH = D / E::VEC;
+    uint4 raw[BT];
+    int64_t slot[BT];
+    // Issue every load of the tile before any arithmetic: BT independent 16-byte loads in flight
+    // per lane, plus the tile's slot indices through the scalar cache.
+#pragma unroll
+    for (int i = 0; i < BT; ++i)
+        if (FULL || i < n) raw[i] = ldrow(xb + i * stride_bytes, lane_off);
+#pragma unroll
+    for (int i = 0; i < BT; ++i)
+        if (FULL || i < n) slot[i] = a.slot[t0 + i];
+    const float inv_d = 1.0f / (float)D;
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+        if (FULL || i < n) {
+            E::widen(raw[i], win[W - 1]);
+            const uint4 out = fused_row<E, W, LPH>(win, p, a.eps, inv_d);
+            if (slot[i] >= 0 && slot[i] < a.num_slots) strow(cache + slot[i] * row_bytes, lane_off, out);
+#pragma unroll
+            for (int k = 0; k + 1 < W; ++k)
+#pragma unroll
+                for (int v = 0; v < E::VEC; ++v) win[k][v] = win[k + 1][v];
+        }
+    }
+}
+
+template <class E, int D, int W, int BT>
+__global__ void __launch_bounds__(kBlock) prefill_kernel(StepArgs a) {
+    constexpr int VEC = E::VEC;
+    constexpr int LPH = D / VEC;
+    constexpr int R = W - 1;
+
+    // XCD-aware remap of the hardware workgroup id (gridDim.x is a multiple of kXcds).
+    const int G = gridDim.x;
+    const int hw = blockIdx.x;
+    const int logical = (hw % kXcds) * (G / kXcds) + hw / kXcds;
+    const int tile = logical / a.lane_blocks;
+    const int lb = logical - tile * a.lane_blocks;
+    if (tile >= a.tiles) return;
+
+    const int lane = lb * kBlock + threadIdx.x;
+    if (lane >= 2 * a.lanes_per_tensor) return;
+    const int tensor = lane >= a.lanes_per_tensor;
+    const int c = lane - tensor * a.lanes_per_tensor;
+    const int h = c / LPH;
+    const int d0 = (c - h * LPH) * VEC;
+    const int64_t T = a.tokens;
+
+    // Which sequence owns this tile: the largest s with P(s) <= tile.
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tile_base<BT>(a.cu, mid, T) <= tile) lo = mid; else hi = mid - 1;
+    }
+    const int s = uniform(lo);
+    const int64_t start = uniform((int64_t)clamp_tok(a.cu[s], T));
+    int64_t end = uniform((int64_t)clamp_tok(a.cu[s + 1], T));
+    if (end < start) end = start;
+    const int64_t L = end - start;
+    const int64_t j = tile - tile_base<BT>(a.cu, s, T);
+    const int64_t ntiles = L > 0 ? (L + BT - 1) / BT : 1;
+    if (j < 0 || j >= ntiles) return;
+
+    const char* x = static_cast<const char*>(a.x[tensor]);
+    const int64_t stride_bytes = a.x_stride[tensor] * E::BYTES;
+    char* cache = static_cast<char*>(a.cache[tensor]);
+    char* state = static_cast<char*>(a.state[tensor]);
+    const int64_t row_bytes = (int64_t)a.heads * D * E::BYTES;
+    const uint32_t lane_off = (uint32_t)(((int64_t)h * D + d0) * E::BYTES);
+
+    LaneParams<E, W> p;
+    load_params<E, W>(a.taps[tensor], a.gamma[tensor], a.heads, D, h, d0, p);
+
+    // Window rows before the tile's first token.
+    float win[W][VEC];
+    int32_t idx = -1;
+    bool slot_ok = false, read_state = false;
+    if (j == 0) {
+        idx = uniform(a.state_idx ? a.state_idx[s] : s);
+        slot_ok = R > 0 && state != nullptr && idx >= 0 && idx < a.num_state_slots;
+        read_state = slot_ok && (a.has_init ? a.has_init[s] != 0 : true);
+    }
+    const int64_t t0 = start + j * BT;
+    const char* state_row = state + (int64_t)idx * R * row_bytes;  // used only when slot_ok
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        uint4 r = make_uint4(0, 0, 0, 0);
+        if (j > 0)
+            r = ldrow(x + (t0 - R + k) * stride_bytes, lane_off);
+        else if (read_state)
+            r = ldrow(state_row + k * row_bytes, lane_off);
+        E::widen(r, win[k]);
+    }
+
+    const int n = (int)((L - j * BT) < BT ? (L - j * BT) : BT);
+    if (n == BT)
+        prefill_tokens<E, D, W, BT, true>(a, p, win, x + t0 * stride_bytes, stride_bytes, cache,
+                                          row_bytes, lane_off, t0, n);
+    else if (n > 0)
+        prefill_tokens<E, D, W, BT, false>(a, p, win, x + t0 * stride_bytes, stride_bytes, cache,
+                                           row_bytes, lane_off, t0, n);
+
+    // The first tile of the sequence writes its new state: row i = e[L + i] where e is the
+    // initial window followed by the sequence's rows. Rows are written in increasing i and row i
+    // may read old row L + i > i, which is therefore still unmodified.
+    if (R > 0 && j == 0 && slot_ok) {
+        char* dst = state + (int64_t)idx * R * row_bytes;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int64_t e = L + i;
+            uint4 r = make_uint4(0, 0, 0, 0);
+            if (e >= R)
+                r = ldrow(x + (start + e - R) * stride_bytes, lane_off);
+            else if (read_state)
+                r = ldrow(dst + e * row_bytes, lane_off);
+            if (e != i || !read_state)  // e == i with a read state is a no-op copy
+                strow(dst + i * row_bytes, lane_off, r);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Decode: one token per sequence; window = [state rows 0..W-2, new row]; state shifts by one.
+// ------------------------------------------------------------------------------------------------
+template <class E, int D, int W>
+__global__ void __launch_bounds__(kBlock) decode_kernel(StepArgs a) {
+    constexpr int VEC = E::VEC;
+    constexpr int LPH = D / VEC;
+    constexpr int R = W - 1;
+    const int64_t b = blockIdx.x;
+    const int lane = blockIdx.y * kBlock + threadIdx.x;
+    if (lane >= 2 * a.lanes_per_tensor) return;
+    const int tensor = lane >= a.lanes_per_tensor;
+    const int c = lane - tensor * a.lanes_per_tensor;
+    const int h = c / LPH;
+    const int d0 = (c - h * LPH) * VEC;
+    const int64_t row_bytes = (int64_t)a.heads * D * E::BYTES;
+    const uint32_t lane_off = (uint32_t)(((int64_t)h * D + d0) * E::BYTES);
+    char* state = static_cast<char*>(a.state[tensor]);
+
+    const int32_t idx = uniform(a.state_idx ? a.state_idx[b] : (int32_t)b);
+    const bool slot_ok = R > 0 && state != nullptr && idx >= 0 && idx < a.num_state_slots;
+    char* srow = state + (int64_t)idx * R * row_bytes;  // used only when slot_ok
+
+    uint4 raw[W];
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+        raw[k] = slot_ok ? ldrow(srow + k * row_bytes, lane_off) : make_uint4(0, 0, 0, 0);
+    raw[R] = ldrow(static_cast<const char*>(a.x[tensor]) + b * a.x_stride[tensor] * E::BYTES,
+                   lane_off);
+    const int64_t slot = a.slot[b];
+
+    LaneParams<E, W> p;
+    load_params<E, W>(a.taps[tensor], a.gamma[tensor], a.heads, D, h, d0, p);
+    float win[W][VEC];
+#pragma unroll
+    for (int k = 0; k < W; ++k) E::widen(raw[k], win[k]);
+    const uint4 out = fused_row<E, W, LPH>(win, p, a.eps, 1.0f / (float)D);
+
+    if (slot >= 0 && slot < a.num_slots)
+        strow(static_cast<char*>(a.cache[tensor]) + slot * row_bytes, lane_off, out);
+    if (slot_ok) {
+#pragma unroll
+        for (int k = 0; k < R; ++k) strow(srow + k * row_bytes, lane_off, raw[k + 1]);
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Dispatch tables: [dtype][head_dim index][width - 1]
+// ------------------------------------------------------------------------------------------------
+using KernelFn = void (*)(StepArgs);
+
+template <class E>
+constexpr int tile_tokens() { return 16; }
+
+template <class E, int D, int W>
+constexpr KernelFn prefill_fn() { return prefill_kernel<E, D, W, tile_tokens<E>()>; }
+template <class E, int D, int W>
+constexpr KernelFn decode_fn() { return decode_kernel<E, D, W>; }
+
+#define SC_ROW(KIND, E, D)                                                                   \
+    { KIND##_fn<E, D, 1>(), KIND##_fn<E, D, 2>(), KIND##_fn<E, D, 3>(), KIND##_fn<E, D, 4>(), \
+      KIND##_fn<E, D, 5>(), KIND##_fn<E, D, 6>(), KIND##_fn<E, D, 7>(), KIND##_fn<E, D, 8>() }
+#define SC_TABLE(KIND)                                                          \
+    {                                                                          \
+        {SC_ROW(KIND, F32, 64), SC_ROW(KIND, F32, 128), SC_ROW(KIND, F32, 256)},    \
+        {SC_ROW(KIND, BF16, 64), SC_ROW(KIND, BF16, 128), SC_ROW(KIND, BF16, 256)}, \
+    }
+
+const KernelFn kPrefill[2][3][8] = SC_TABLE(prefill);
+const KernelFn kDecode[2][3][8] = SC_TABLE(decode);
+
+int d_index(int D) { return D == 64 ? 0 : (D == 128 ? 1 : 2); }
+
+}  // namespace
+
+int prefill_tile_tokens(int dtype, int, int) {
+    return dtype == 0 ? tile_tokens<F32>() : tile_tokens<BF16>();
+}
+
+hipError_t launch_prefill(StepArgs a, int dtype, int head_dim, int width, hipStream_t stream) {
+    const int64_t lanes = 2 * (int64_t)a.lanes_per_tensor;
+    const int block = lanes >= kBlock ? kBlock : (int)((lanes + 63) / 64 * 64);
+    const int64_t total = (int64_t)a.tiles * a.lane_blocks;
+    const int64_t grid = (total + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL(kPrefill[dtype][d_index(head_dim)][width - 1], dim3((unsigned)grid),
+                       dim3(block), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(StepArgs a, int dtype, int head_dim, int width, hipStream_t stream) {
+    const int64_t lanes = 2 * (int64_t)a.lanes_per_tensor;
+    const int block = lanes >= kBlock ? kBlock : (int)((lanes + 63) / 64 * 64);
+    hipLaunchKernelGGL(kDecode[dtype][d_index(head_dim)][width - 1],
+                       dim3((unsigned)a.tokens, (unsigned)a.lane_blocks), dim3(block), 0, stream,
+                       a);
+    return hipGetLastError();
+}
+
+}  // namespace sc

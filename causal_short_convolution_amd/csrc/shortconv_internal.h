@@ -1,0 +1,45 @@
+// Internal interface between the C-ABI layer (abi.hip) and the kernels (kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sc {
+
+// Device-side arguments of one fused step. Index [0] is K, [1] is V.
+struct StepArgs {
+    const void* x[2];        // new rows, [tokens][H][D] with token stride x_stride[i] elements
+    int64_t x_stride[2];
+    const float* taps[2];    // fp32 [W][H][D]
+    const float* gamma[2];   // fp32 [D]
+    void* state[2];          // [num_state_slots][W-1][H][D] or null (W == 1)
+    void* cache[2];          // [num_slots][H][D]
+    const int32_t* cu;       // prefill: int32 [num_seqs+1]
+    const int32_t* state_idx;  // int32 [num_seqs] or null (identity)
+    const uint8_t* has_init;   // prefill: uint8 [num_seqs] or null (all 1)
+    const int64_t* slot;       // int64 [tokens]
+    int64_t tokens;            // prefill: total packed tokens; decode: batch
+    int64_t num_slots;
+    int64_t num_state_slots;
+    int32_t num_seqs;          // prefill only
+    int32_t heads;
+    int32_t lanes_per_tensor;  // heads * head_dim / (16 / element bytes)
+    int32_t lane_blocks;       // blocks needed to cover 2 * lanes_per_tensor lanes
+    int32_t tiles;             // prefill: number of logical tiles (upper bound, see kernels.hip)
+    float eps;
+};
+
+// Launch geometry chosen by the kernels for a given problem.
+struct Launch {
+    dim3 grid;
+    dim3 block;
+};
+
+// Returns hipSuccess or the launch error. `dtype`: 0 = fp32, 1 = bf16. Shapes already validated.
+hipError_t launch_prefill(StepArgs a, int dtype, int head_dim, int width, hipStream_t stream);
+hipError_t launch_decode(StepArgs a, int dtype, int head_dim, int width, hipStream_t stream);
+
+// Tokens per prefill tile for a (dtype, head_dim, width) combination.
+int prefill_tile_tokens(int dtype, int head_dim, int width);
+
+}  // namespace sc

@@ -1,0 +1,134 @@
+/*
+ * shortconv.h -- C ABI of the fused ShortConv K/V step for AMD Instinct MI355X (gfx950).
+ *
+ * The step (aib.vote English news item "SGLang and Miles ... day-0 support for Inkling",
+ * paragraphs 1-2: ShortConv is a causal convolution over the token dimension, and its fused
+ * kernel combines the K/V convolution, a normalization and the KV-cache write), for each of K and
+ * V with its own taps and gamma:
+ *
+ *   window    the current row and the W-1 rows before it in the same sequence (axbrief.com blog
+ *             on Inkling's specifications, section on SConv and MoE); rows before the start of a
+ *             sequence come from its conv state, or are zero for a fresh sequence;
+ *   conv      c[h,d] = sum_{k=0}^{W-1} taps[k,h,d] * window[k][h,d]   (fp32 accumulation in
+ *             order k = 0..W-1; window[W-1] is the current row, window[0] the oldest);
+ *   norm      y[h,d] = c[h,d] / sqrt(mean_d c[h,:]^2 + eps) * gamma[d]  (RMSNorm over head_dim
+ *             per (token, head), one gamma per tensor shared by all heads);
+ *   write     cache[slot_mapping[t], h, d] = y[h,d] rounded once (to nearest even) to the element
+ *             type, skipped when the slot is outside [0, num_slots);
+ *   state     the sequence's conv state becomes its W-1 most recent raw rows (bit copies, oldest
+ *             first), the per-request state pool of the serving engine (data-sketchers.com SGLang
+ *             cookbook for Inkling-Small, section 2, memory-pool ratios).
+ *
+ * Conventions for every entry point:
+ *  - Element type `dtype` (SC_DTYPE_F32 or SC_DTYPE_BF16) applies to K, V, the conv state and the
+ *    caches alike. Taps and gamma are always fp32.
+ *  - Layouts (all row-major, innermost dimension last, H = num_heads, D = head_dim):
+ *      K, V          [tokens][H][D], token stride given in elements (>= H*D), rows 16-byte aligned;
+ *      taps          fp32 [W][H][D] contiguous;   gamma fp32 [D];
+ *      conv state    [num_state_slots][W-1][H][D] contiguous, row 0 = oldest;
+ *      caches        [num_slots][H][D] contiguous (one paged-cache row per slot).
+ *  - Every pointer except `stream` is a device pointer owned by the caller. The library never
+ *    allocates, frees or synchronizes; it launches on `stream` (a hipStream_t, NULL = the null
+ *    stream) and returns before the work is done.
+ *  - Return value: SC_OK (0), or a negative SC_ERR_* code; shortconv_last_error() then describes
+ *    it. Arguments are validated on the host before anything is launched. The contents of device
+ *    index arrays are not read by the host; the kernels clamp them so that no invalid index is
+ *    ever dereferenced (see each entry point).
+ *  - Supported shapes: head_dim in {64, 128, 256}; 1 <= width <= 8; num_heads >= 1.
+ *  - K/V and the cache or state must not overlap. Two calls that share a cache or state buffer
+ *    must be ordered by the caller (same stream, or events).
+ */
+#ifndef SHORTCONV_H
+#define SHORTCONV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SHORTCONV_ABI_VERSION 1
+
+typedef enum {
+    SC_DTYPE_F32 = 0,  /* IEEE binary32 */
+    SC_DTYPE_BF16 = 1, /* bfloat16 (upper half of binary32), conversion rounds to nearest even */
+} sc_dtype_t;
+
+enum {
+    SC_OK = 0,
+    SC_ERR_INVALID = -1,     /* a null required pointer, a negative size, a bad stride */
+    SC_ERR_UNSUPPORTED = -2, /* head_dim, width or dtype outside what the library is built for */
+    SC_ERR_HIP = -3,         /* the HIP runtime refused the launch */
+};
+
+/*
+ * Prefill over packed variable-length sequences.
+ *
+ *  k, v                [total_tokens][H][D] new projected rows of all sequences, packed in
+ *                      sequence order; k_tok_stride / v_tok_stride in elements.
+ *  cu_seqlens          int32 [num_seqs+1], cu_seqlens[0] = 0, non-decreasing, last = total_tokens.
+ *                      Sequence s owns tokens [cu_seqlens[s], cu_seqlens[s+1]). Zero-length
+ *                      sequences are allowed (their state is still rewritten, see below).
+ *                      The kernel clamps every entry into [0, total_tokens].
+ *  k_taps, v_taps      fp32 [W][H][D];  k_gamma, v_gamma fp32 [D];  eps >= 0 (e.g. 1e-6).
+ *  k_state, v_state    [num_state_slots][W-1][H][D], read and rewritten in place. May be NULL
+ *                      only when width == 1 (then num_state_slots is ignored).
+ *  state_idx           int32 [num_seqs]: pool row of sequence s, or NULL for row s. Entries must
+ *                      be distinct. An entry outside [0, num_state_slots) means the sequence has no
+ *                      state row: its window starts from zeros and nothing is written back.
+ *  has_initial_state   uint8 [num_seqs], or NULL for "all 1". 1 = the window before the first
+ *                      token is the stored state row (a resumed sequence or chunk); 0 = zeros (a
+ *                      fresh sequence). The new state is written in both cases: the last W-1 rows
+ *                      of [initial window, new rows], so a sequence shorter than W-1 keeps the
+ *                      newest surviving old rows ahead of its own.
+ *  slot_mapping        int64 [total_tokens]: cache row of each token; a value outside
+ *                      [0, num_slots) (e.g. -1 for padding) means the row is not written.
+ *                      Non-negative entries must be distinct.
+ *  k_cache, v_cache    [num_slots][H][D] written at the mapped rows only.
+ *
+ * total_tokens == 0 with num_seqs == 0 returns SC_OK without launching.
+ */
+int shortconv_kv_prefill(const void* k, const void* v, int64_t k_tok_stride, int64_t v_tok_stride,
+                         const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                         const float* k_taps, const float* v_taps, const float* k_gamma,
+                         const float* v_gamma, float eps, void* k_state, void* v_state,
+                         int64_t num_state_slots, const int32_t* state_idx,
+                         const uint8_t* has_initial_state, const int64_t* slot_mapping,
+                         void* k_cache, void* v_cache, int64_t num_slots, int32_t num_heads,
+                         int32_t head_dim, int32_t width, int32_t dtype, void* stream);
+
+/*
+ * Decode: one new token for each of `batch` sequences, each resuming from its conv state.
+ *
+ *  k_new, v_new        [batch][H][D] (token strides in elements).
+ *  k_state, v_state    [num_state_slots][W-1][H][D]; sequence b reads rows 0..W-2 of
+ *                      pool row state_idx[b] as the past of its window and then shifts the pool
+ *                      row by one (rows 1..W-2 move up, the new raw row goes last). NULL only when
+ *                      width == 1.
+ *  state_idx           int32 [batch], or NULL for row b. Distinct. Out-of-pool entries: zeros as
+ *                      the past, no write-back.
+ *  slot_mapping        int64 [batch]: cache row of each new token (outside [0, num_slots) = skip).
+ *
+ * The result is bit-identical to shortconv_kv_prefill called with one token per sequence and
+ * has_initial_state = 1. batch == 0 returns SC_OK without launching.
+ */
+int shortconv_kv_decode(const void* k_new, const void* v_new, int64_t k_tok_stride,
+                        int64_t v_tok_stride, int32_t batch, const float* k_taps,
+                        const float* v_taps, const float* k_gamma, const float* v_gamma, float eps,
+                        void* k_state, void* v_state, int64_t num_state_slots,
+                        const int32_t* state_idx, const int64_t* slot_mapping, void* k_cache,
+                        void* v_cache, int64_t num_slots, int32_t num_heads, int32_t head_dim,
+                        int32_t width, int32_t dtype, void* stream);
+
+/* Message for the last non-zero return on the calling thread ("" if none). Valid until the next
+ * call on the same thread. */
+const char* shortconv_last_error(void);
+
+/* SHORTCONV_ABI_VERSION of the built library. */
+int shortconv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHORTCONV_H */

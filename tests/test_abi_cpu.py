@@ -1,0 +1,158 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every symbol include/shortconv.h
+declares, and rejects bad arguments before anything reaches the HIP runtime.
+
+Pointer arguments here are fake integers; every call either fails validation or returns SC_OK
+without launching, so none is ever dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "shortconv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from causal_short_convolution_amd import _binding
+    if not os.path.exists(_binding.LIBRARY_PATH):
+        from causal_short_convolution_amd import build
+        build.build()
+    return _binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(shortconv_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["shortconv_abi_version", "shortconv_kv_decode",
+                                    "shortconv_kv_prefill", "shortconv_last_error"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from causal_short_convolution_amd import _binding
+    out = subprocess.run(["nm", "-D", "--defined-only", _binding.LIBRARY_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    # nothing else with code is exported: the boundary is the header
+    assert exported == set(declared_functions())
+
+
+def test_abi_version(lib):
+    text = open(HEADER).read()
+    v = int(re.search(r"#define SHORTCONV_ABI_VERSION (\d+)", text).group(1))
+    assert lib.shortconv_abi_version() == v
+
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced
+
+
+def prefill_args(**over):
+    a = dict(k=FAKE, v=FAKE, ks=1024, vs=1024, cu=FAKE, n=2, T=10, kt=FAKE, vt=FAKE, kg=FAKE,
+             vg=FAKE, eps=1e-6, kst=FAKE, vst=FAKE, S=2, sidx=FAKE, hinit=FAKE, slot=FAKE,
+             kc=FAKE, vc=FAKE, slots=100, H=8, D=128, W=4, dtype=1, stream=None)
+    a.update(over)
+    return [a[k] for k in ("k", "v", "ks", "vs", "cu", "n", "T", "kt", "vt", "kg", "vg", "eps",
+                           "kst", "vst", "S", "sidx", "hinit", "slot", "kc", "vc", "slots", "H",
+                           "D", "W", "dtype", "stream")]
+
+
+def decode_args(**over):
+    a = dict(k=FAKE, v=FAKE, ks=1024, vs=1024, B=3, kt=FAKE, vt=FAKE, kg=FAKE, vg=FAKE, eps=1e-6,
+             kst=FAKE, vst=FAKE, S=3, sidx=FAKE, slot=FAKE, kc=FAKE, vc=FAKE, slots=100, H=8,
+             D=128, W=4, dtype=1, stream=None)
+    a.update(over)
+    return [a[k] for k in ("k", "v", "ks", "vs", "B", "kt", "vt", "kg", "vg", "eps", "kst", "vst",
+                           "S", "sidx", "slot", "kc", "vc", "slots", "H", "D", "W", "dtype",
+                           "stream")]
+
+
+INVALID, UNSUPPORTED = -1, -2
+
+PREFILL_CASES = [
+    (dict(dtype=7), UNSUPPORTED, "dtype"),
+    (dict(D=96), UNSUPPORTED, "head_dim"),
+    (dict(W=0), UNSUPPORTED, "width"),
+    (dict(W=9), UNSUPPORTED, "width"),
+    (dict(H=0), INVALID, "num_heads"),
+    (dict(k=None), INVALID, "null K"),
+    (dict(vt=None), INVALID, "taps"),
+    (dict(slot=None), INVALID, "slot_mapping"),
+    (dict(kc=None), INVALID, "cache"),
+    (dict(kst=None), INVALID, "conv state"),
+    (dict(n=-1), INVALID, "num_seqs"),
+    (dict(T=-5), INVALID, "total_tokens"),
+    (dict(T=1 << 31), INVALID, "total_tokens"),
+    (dict(cu=None), INVALID, "cu_seqlens"),
+    (dict(ks=1000), INVALID, "stride"),
+    (dict(vs=1028, dtype=1), INVALID, "16 bytes"),
+    (dict(k=FAKE + 8), INVALID, "aligned"),
+    (dict(eps=-1.0), INVALID, "eps"),
+    (dict(eps=float("nan")), INVALID, "eps"),
+    (dict(slots=-1), INVALID, "num_slots"),
+    (dict(S=-1), INVALID, "num_state_slots"),
+]
+
+
+@pytest.mark.parametrize("over,code,msg", PREFILL_CASES, ids=[c[2] + str(i) for i, c in
+                                                               enumerate(PREFILL_CASES)])
+def test_prefill_rejects(lib, over, code, msg):
+    rc = lib.shortconv_kv_prefill(*prefill_args(**over))
+    assert rc == code
+    err = lib.shortconv_last_error().decode()
+    assert err.startswith("shortconv_kv_prefill") and msg in err, err
+
+
+DECODE_CASES = [
+    (dict(dtype=2), UNSUPPORTED, "dtype"),
+    (dict(D=32), UNSUPPORTED, "head_dim"),
+    (dict(B=-1), INVALID, "batch"),
+    (dict(kc=None), INVALID, "cache"),
+    (dict(vst=None), INVALID, "conv state"),
+    (dict(ks=64, D=128, H=1, dtype=0), INVALID, "stride"),
+]
+
+
+@pytest.mark.parametrize("over,code,msg", DECODE_CASES, ids=[c[2] + str(i) for i, c in
+                                                             enumerate(DECODE_CASES)])
+def test_decode_rejects(lib, over, code, msg):
+    rc = lib.shortconv_kv_decode(*decode_args(**over))
+    assert rc == code
+    assert msg in lib.shortconv_last_error().decode()
+
+
+def test_empty_work_returns_ok_without_launch(lib):
+    # no sequences; no decodes; width 1 with no tokens: nothing to launch, no HIP call made
+    assert lib.shortconv_kv_prefill(*prefill_args(n=0, T=0, k=None, v=None, slot=None,
+                                                  cu=None)) == 0
+    assert lib.shortconv_kv_decode(*decode_args(B=0, k=None, v=None, slot=None)) == 0
+    assert lib.shortconv_kv_prefill(*prefill_args(W=1, T=0, kst=None, vst=None)) == 0
+    assert lib.shortconv_last_error().decode() == ""
+
+
+def test_state_may_be_null_for_width_one_or_empty_pool(lib):
+    # validation only: these fail later on something else (unsupported head_dim) rather than on
+    # the missing state, proving the state check accepts them
+    rc = lib.shortconv_kv_prefill(*prefill_args(W=1, kst=None, vst=None, D=48))
+    assert rc == UNSUPPORTED
+    rc = lib.shortconv_kv_prefill(*prefill_args(S=0, kst=None, vst=None, eps=-1.0))
+    assert rc == INVALID and "eps" in lib.shortconv_last_error().decode()
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path):
+    from causal_short_convolution_amd import _binding
+    saved = _binding._lib
+    _binding._lib = None
+    try:
+        with pytest.raises(ImportError, match="not built"):
+            _binding.load_library(str(tmp_path / "missing.so"))
+    finally:
+        _binding._lib = saved

@@ -1,0 +1,276 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, plus the invariants that
+must hold bit for bit on the device.
+
+Bars: cache rows within the stated float tolerance (oracle.compare), untouched cache rows and the
+whole conv-state pool bit-exact. Every case runs the library exactly as the bench does.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_harness import DEV, DeviceWorkload, judge, to_dev, to_host, rows_to_dev
+from causal_short_convolution_amd import (ShortConvError, shortconv_kv_decode,
+                                          shortconv_kv_prefill)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run_and_judge(w):
+    dw = DeviceWorkload(w)
+    dw.run()
+    return judge(dw)
+
+
+# ------------------------------------------------------------------------------------------------
+# The five reference workloads at full size
+# ------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_reference_workload(n):
+    w = workloads.config(n)
+    rep = _run_and_judge(w)
+    print(f"config {n} ({w.name}): rows={rep['rows']} worst={rep['worst']:.3f} "
+          f"max_rel_well_conditioned={rep['max_rel_well_conditioned']:.3e}", flush=True)
+    assert rep["rows"] == w.tokens
+
+
+# ------------------------------------------------------------------------------------------------
+# Shapes, ragged packing and edge cases, small enough for the oracle to check every element
+# ------------------------------------------------------------------------------------------------
+LENS = [0, 1, 2, 3, 15, 16, 17, 31, 33, 100, 0, 5]
+SMALL = [(dt, H, D, W) for dt in ("f32", "bf16") for (H, D) in ((1, 64), (3, 128), (2, 256))
+         for W in (1, 2, 4, 8)]
+
+
+@pytest.mark.parametrize("dt,H,D,W", SMALL, ids=[f"{a}-H{b}-D{c}-W{d}" for a, b, c, d in SMALL])
+def test_small_ragged(dt, H, D, W):
+    hin = [(i * 7) % 3 != 0 for i in range(len(LENS))]
+    spec = workloads.Spec(dtype=dt, H=H, D=D, W=W, seed=100 + W, prefill_lens=LENS, has_init=hin,
+                          decode_ctx=[5, 1, 70], block_size=16, pad_slot_every=9, spare_slots=40)
+    _run_and_judge(workloads.build(spec))
+
+
+def test_strided_inputs_and_many_heads():
+    spec = workloads.Spec(dtype="bf16", H=40, D=128, W=4, seed=9, prefill_lens=[37, 300, 1],
+                          has_init=[1, 0, 1], decode_ctx=[9, 12], token_pad=24)
+    _run_and_judge(workloads.build(spec))
+
+
+def test_many_short_sequences():
+    g = np.random.default_rng(3)
+    lens = g.integers(0, 6, size=700).tolist()
+    spec = workloads.Spec(dtype="bf16", H=8, D=128, W=5, seed=4, prefill_lens=lens,
+                          has_init=(g.random(700) < 0.5).tolist())
+    _run_and_judge(workloads.build(spec))
+
+
+def test_outliers_and_zero_rows():
+    spec = workloads.Spec(dtype="bf16", H=8, D=128, W=8, seed=12, prefill_lens=[500, 20],
+                          has_init=[0, 1], outlier_p=0.05, outlier_mul=50.0)
+    w = workloads.build(spec)
+    st = w.steps[0]
+    st.k[100:110] = 0          # whole zero rows: c = 0, output must be exactly 0
+    st.v[200:230, 3] = 0
+    _run_and_judge(w)
+
+
+def test_all_sequences_empty_still_update_state():
+    spec = workloads.Spec(dtype="f32", H=2, D=64, W=4, seed=2, prefill_lens=[0, 0, 0],
+                          has_init=[1, 0, 1])
+    _run_and_judge(workloads.build(spec))
+
+
+def test_out_of_pool_state_index_and_slots():
+    spec = workloads.Spec(dtype="bf16", H=2, D=128, W=4, seed=21, prefill_lens=[20, 7, 9],
+                          has_init=[1, 1, 1], decode_ctx=[3, 4])
+    w = workloads.build(spec)
+    w.steps[0].state_idx[1] = 10_000        # no such state row: zeros in, nothing written
+    w.steps[1].state_idx[0] = -3
+    w.steps[0].slot_mapping[[2, 5]] = [-1, w.num_slots + 7]   # skipped
+    w.steps[1].slot_mapping[1] = 1 << 40
+    _run_and_judge(w)
+
+
+def test_width_one_without_state():
+    spec = workloads.Spec(dtype="bf16", H=4, D=64, W=1, seed=5, prefill_lens=[9, 0, 40],
+                          decode_ctx=[2])
+    w = workloads.build(spec)
+    assert w.k_state is None
+    _run_and_judge(w)
+
+
+def test_non_default_stream():
+    w = workloads.build(workloads.Spec(dtype="bf16", H=8, D=128, W=4, seed=6,
+                                       prefill_lens=[300, 41], has_init=[0, 1], decode_ctx=[8]))
+    dw = DeviceWorkload(w)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dw.run(stream=s)
+    s.synchronize()
+    judge(dw)
+
+
+def test_empty_calls_are_noops():
+    w = workloads.config(1)
+    dw = DeviceWorkload(w)
+    e_rows = torch.empty((0, 1, 64), dtype=torch.float32, device=DEV)
+    e_i64 = torch.empty(0, dtype=torch.int64, device=DEV)
+    e_i32 = torch.empty(0, dtype=torch.int32, device=DEV)
+    shortconv_kv_decode(e_rows, e_rows, dw.k_taps, dw.v_taps, dw.k_gamma, dw.v_gamma, w.eps,
+                        dw.k_state, dw.v_state, e_i32, e_i64, dw.k_cache, dw.v_cache)
+    shortconv_kv_prefill(e_rows, e_rows, torch.zeros(1, dtype=torch.int32, device=DEV), dw.k_taps,
+                         dw.v_taps, dw.k_gamma, dw.v_gamma, w.eps, dw.k_state, dw.v_state, e_i32,
+                         None, e_i64, dw.k_cache, dw.v_cache)
+    torch.cuda.synchronize()
+    judge(dw, results=[oracle.StepResult(*(np.zeros((0, 1, 64)),) * 4, np.zeros(0, np.int64),
+                                         w.k_state, w.v_state)])
+
+
+def test_rejects_bad_arguments_without_launch():
+    w = workloads.config(1)
+    dw = DeviceWorkload(w)
+    d = dw.steps[0]
+    with pytest.raises(ShortConvError, match="SC_ERR_UNSUPPORTED"):
+        bad_taps = torch.zeros((9, 1, 64), dtype=torch.float32, device=DEV)
+        shortconv_kv_prefill(d["k"], d["v"], d["cu"], bad_taps, bad_taps, dw.k_gamma, dw.v_gamma,
+                             w.eps, dw.k_state, dw.v_state, d["sidx"], d["hinit"], d["slot"],
+                             dw.k_cache, dw.v_cache)
+    torch.cuda.synchronize()
+    judge(dw, results=[oracle.StepResult(*(np.zeros((0, 1, 64)),) * 4, np.zeros(0, np.int64),
+                                         w.k_state, w.v_state)])
+
+
+# ------------------------------------------------------------------------------------------------
+# Bit-exact invariants on the device
+# ------------------------------------------------------------------------------------------------
+def _prefill_out(w, k=None, state=None, hinit=None, eps=None, taps=None):
+    """Run one prefill of workload w on the device; return (K rows in token order, K state)."""
+    st = w.steps[0]
+    k = st.k if k is None else k
+    T, H, D = k.shape
+    kk = rows_to_dev(k)
+    taps_d = to_dev(w.k_taps if taps is None else taps)
+    cache = torch.zeros((T, H, D), dtype=kk.dtype, device=DEV)
+    ks = to_dev(w.k_state if state is None else state)
+    ks2 = None if ks is None else ks.clone()
+    shortconv_kv_prefill(kk, kk, to_dev(st.cu_seqlens), taps_d, taps_d, to_dev(w.k_gamma),
+                         to_dev(w.k_gamma), w.eps if eps is None else eps, ks, ks2,
+                         to_dev(st.state_idx), to_dev(st.has_init if hinit is None else hinit),
+                         torch.arange(T, dtype=torch.int64, device=DEV), cache, cache.clone())
+    torch.cuda.synchronize()
+    return to_host(cache, w.dtype), (None if ks is None else to_host(ks, w.dtype))
+
+
+def _small(dtype="bf16", W=4, lens=(70, 3, 0, 40), hin=(1, 0, 1, 1), seed=5, H=8, D=128):
+    return workloads.build(workloads.Spec(dtype=dtype, H=H, D=D, W=W, seed=seed,
+                                          prefill_lens=list(lens), has_init=list(hin)))
+
+
+@pytest.mark.parametrize("dtype,W", [("bf16", 4), ("f32", 8), ("bf16", 2)])
+def test_decode_equals_prefill_bitwise(dtype, W):
+    w = _small(dtype=dtype, W=W, lens=(21, 2, 5), hin=(1, 1, 1))
+    st = w.steps[0]
+    y0, s0 = _prefill_out(w)
+    H, D = w.H, w.D
+    taps, gam = to_dev(w.k_taps), to_dev(w.k_gamma)
+    ks = to_dev(w.k_state)
+    cache = torch.zeros((st.tokens, H, D), dtype=ks.dtype, device=DEV)
+    for s in range(st.num_seqs):
+        for t in range(int(st.cu_seqlens[s]), int(st.cu_seqlens[s + 1])):
+            x = rows_to_dev(st.k[t:t + 1])
+            shortconv_kv_decode(x, x, taps, taps, gam, gam, w.eps, ks, ks.clone(),
+                                to_dev(st.state_idx[s:s + 1]),
+                                torch.tensor([t], dtype=torch.int64, device=DEV), cache,
+                                cache.clone())
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(cache, dtype), y0), "decode output != prefill output"
+    assert np.array_equal(to_host(ks, dtype), s0), "decode state != prefill state"
+
+
+def test_chunked_equals_oneshot_bitwise():
+    w = _small(W=4, lens=(200, 37), hin=(1, 0))
+    st = w.steps[0]
+    y0, s0 = _prefill_out(w)
+    taps, gam = to_dev(w.k_taps), to_dev(w.k_gamma)
+    ks = to_dev(w.k_state)
+    H, D = w.H, w.D
+    cache = torch.zeros((st.tokens, H, D), dtype=ks.dtype, device=DEV)
+    for s in range(2):
+        a, b = int(st.cu_seqlens[s]), int(st.cu_seqlens[s + 1])
+        pos, first = a, True
+        for chunk in (1, 2, 16, 17, 5, 1000):
+            e = min(b, pos + chunk)
+            x = rows_to_dev(st.k[pos:e])
+            hin = torch.tensor([1 if not first else int(st.has_init[s])], dtype=torch.uint8,
+                               device=DEV)
+            shortconv_kv_prefill(x, x, torch.tensor([0, e - pos], dtype=torch.int32, device=DEV),
+                                 taps, taps, gam, gam, w.eps, ks, ks.clone(),
+                                 to_dev(st.state_idx[s:s + 1]), hin,
+                                 torch.arange(pos, e, dtype=torch.int64, device=DEV), cache,
+                                 cache.clone())
+            pos, first = e, False
+            if pos == b:
+                break
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(cache, "bf16"), y0)
+    assert np.array_equal(to_host(ks, "bf16"), s0)
+
+
+def test_delta_taps_are_exact_shifts():
+    w = _small(dtype="f32", W=4, lens=(50, 2, 9), hin=(1, 1, 0), H=2, D=64)
+    st = w.steps[0]
+    ones = np.ones((1, 2, 64), np.float32)
+    for k in range(4):
+        taps = np.zeros((4, 2, 64), np.float32)
+        taps[k] = 1.0
+        y, _ = _prefill_out(w, taps=taps)
+        for s in range(st.num_seqs):
+            a, b = int(st.cu_seqlens[s]), int(st.cu_seqlens[s + 1])
+            z = (w.k_state[st.state_idx[s]] if st.has_init[s]
+                 else np.zeros((3, 2, 64), np.float32))
+            e = np.concatenate([z, st.k[a:b]], axis=0)
+            w1 = workloads.Workload("w1", "f32", 2, 64, 1, w.eps, ones, ones, w.k_gamma,
+                                    w.k_gamma, len(e), 16, None, None,
+                                    [workloads.Step("prefill", e, e, np.arange(len(e)),
+                                                    np.array([0], np.int32),
+                                                    np.array([0, len(e)], np.int32),
+                                                    np.array([0], np.uint8))])
+            y1, _ = _prefill_out(w1, taps=ones)
+            assert np.array_equal(y[a:b], y1[k:k + b - a]), f"tap {k}, sequence {s}"
+
+
+def test_causality_bitwise():
+    w = _small()
+    st = w.steps[0]
+    y0, _ = _prefill_out(w)
+    for p in (0, 15, 16, 47, 68):
+        k2 = st.k.copy()
+        k2[p + 1:70] ^= np.uint16(0x0040)
+        y1, _ = _prefill_out(w, k=k2)
+        assert np.array_equal(y1[:p + 1], y0[:p + 1]), f"output <= {p} saw the future"
+        assert np.array_equal(y1[70:], y0[70:]), "another sequence changed"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scale_invariance_bitwise(dtype):
+    w = _small(dtype=dtype, lens=(40, 9), hin=(1, 1))
+    st = w.steps[0]
+    y0, _ = _prefill_out(w, eps=0.0)
+    for j in (-6, 5):
+        if dtype == "f32":
+            k2 = st.k * np.float32(2.0 ** j)
+            s2 = w.k_state * np.float32(2.0 ** j)
+        else:  # add j to the bf16 exponent field (no overflow or subnormal at these scales)
+            k2 = workloads.to_bf16_bits(workloads.bf16_bits_to_f32(st.k) * np.float32(2.0 ** j))
+            s2 = workloads.to_bf16_bits(workloads.bf16_bits_to_f32(w.k_state) *
+                                        np.float32(2.0 ** j))
+        y1, _ = _prefill_out(w, k=k2, state=s2, eps=0.0)
+        assert np.array_equal(y0, y1), f"not scale invariant at 2^{j}"
