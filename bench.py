@@ -9,10 +9,14 @@ arithmetic, paged cache with 16-token blocks). Inputs are resident in HBM before
 The batch is replicated into enough distinct device buffers that consecutive steps never find
 their data in the 256 MB Infinity Cache; step i uses replica i mod R.
 
+The K timed launches are captured once into a HIP graph and replayed (host launch cost would
+otherwise pace short kernels); --eager launches them from Python instead.
+
 Prints ONE JSON line: tokens/s over the timed steps (wall clock between two device
-synchronizations), the average duration of the fused kernel from HIP events recorded around each
-launch on the launch stream, algorithmic HBM bytes / that duration against the 8 TB/s peak, the
-same for the decode step (256 sequences x 1 token), and the fp64 CPU oracle timed on host cores.
+synchronizations), the average duration of one fused launch (device time between HIP events
+recorded on the launch stream before the first and after the last launch, divided by K),
+algorithmic HBM bytes / that duration against the 8 TB/s peak, the same for the decode step
+(256 sequences x 1 token), and the fp64 CPU oracle timed on host cores.
 
 Profiling helpers (run under rocprofv3, then summarize):
     --calibrate-copy         also run a plain device copy of known size (counter calibration)
@@ -77,6 +81,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline sample")
+    ap.add_argument("--eager", action="store_true", help="launch from Python instead of a graph")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-profile", default=None, metavar="DIR")
     return ap.parse_args()
@@ -149,47 +154,59 @@ def launcher(w, d):
         d["v_state"], d["sidx"], d["slot"], d["k_cache"], d["v_cache"])
 
 
-def time_steps(torch, fns, steps, warmup):
-    """Warm up, then time exactly `steps` launches: wall clock between two synchronizations, and
-    each launch's duration from a pair of events on the launch (current) stream."""
+def time_steps(torch, fns, steps, warmup, graph=True):
+    """Warm up, then time exactly `steps` launches (step i runs replica i mod R).
+
+    graph=True: the `steps` launches are captured once into a HIP graph (torch.cuda.CUDAGraph)
+    and the timed region is one replay, so host-side launch cost does not pace the device;
+    graph=False: plain launches from Python. Returns (wall seconds between two device
+    synchronizations, device milliseconds between events recorded on the launch stream
+    before the first and after the last launch)."""
     for i in range(warmup):
         fns[i % len(fns)]()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        ev[i][0].record()
-        fns[i % len(fns)]()
-        ev[i][1].record()
-    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fns[i % len(fns)]()
+        g.replay()  # untimed: first replay uploads the graph
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        g.replay()
+        end.record()
+        torch.cuda.synchronize()
+    else:
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            fns[i % len(fns)]()
+        end.record()
+        torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = [a.elapsed_time(b) for a, b in ev]
-    return wall, kernel_ms
+    return wall, start.elapsed_time(end)
 
 
-def measure(torch, w, steps, warmup, reseed=None):
+def measure(torch, w, steps, warmup, reseed=None, graph=True):
     step = w.steps[0]
     alg = algorithmic_bytes(w, step)
     n_rep = max(2, math.ceil(2 * MALL_BYTES / alg) + 1)
     reps = device_replicas(w, torch, n_rep, reseed)
     fns = [launcher(w, d) for d in reps]
-    wall, kms = time_steps(torch, fns, steps, warmup)
-    kms_sorted = sorted(kms)
-    mean_ms = sum(kms) / len(kms)
+    wall, dev_ms = time_steps(torch, fns, steps, warmup, graph)
+    per_launch_ms = dev_ms / steps
     return {
         "tokens_per_step": step.tokens,
         "replicas": n_rep,
+        "launch": "hip graph replay" if graph else "eager",
         "wall_s": wall,
         "ms_per_step": 1e3 * wall / steps,
         "tokens_per_s": step.tokens * steps / wall,
-        "kernel_us_mean": 1e3 * mean_ms,
-        "kernel_us_p10": 1e3 * kms_sorted[len(kms) // 10],
-        "kernel_us_p50": 1e3 * kms_sorted[len(kms) // 2],
-        "kernel_us_p90": 1e3 * kms_sorted[(9 * len(kms)) // 10],
+        "kernel_us_mean": 1e3 * per_launch_ms,
         "algorithmic_bytes": alg,
-        "achieved_GBps": alg / (mean_ms * 1e-3) / 1e9,
+        "achieved_GBps": alg / (per_launch_ms * 1e-3) / 1e9,
     }
 
 
@@ -287,12 +304,13 @@ def main():
         raise SystemExit("bench.py: the mixed workload is measured by its two steps separately")
     main_m = measure(torch, w, args.steps, args.warmup,
                      reseed=(lambda r: workloads.config(n, seed=args.seed + 1000 * r))
-                     if w.steps[0].kind == "decode" else None)
+                     if w.steps[0].kind == "decode" else None, graph=not args.eager)
     extra = {}
     if not args.no_decode and args.workload != "decode":
         wd = workloads.config(3, seed=args.seed)
         dm = measure(torch, wd, args.steps, args.warmup,
-                     reseed=lambda r: workloads.config(3, seed=args.seed + 1000 * r))
+                     reseed=lambda r: workloads.config(3, seed=args.seed + 1000 * r),
+                     graph=not args.eager)
         extra["decode"] = {"workload": "decode", "recipe": wd.recipe, **_round(dm),
                            "frac_of_hbm_peak": dm["achieved_GBps"] / HBM_PEAK_GBPS}
     if args.calibrate_copy:
@@ -331,7 +349,7 @@ def main():
                      "kernel": "prefill_kernel" if st.kind == "prefill" else "decode_kernel",
                      "algorithmic_bytes_per_launch": main_m["algorithmic_bytes"],
                      "kernel_us_mean": main_m["kernel_us_mean"],
-                     "kernel_us_p50": main_m["kernel_us_p50"]},
+                     "launch": main_m["launch"]},
         **extra,
     }
     if not args.no_cpu_baseline:
