@@ -13,23 +13,24 @@
 // wavefront covers 64 * 16 B = 1 KiB of a row, so every global load and store is a fully used,
 // contiguous 16-byte-per-lane access. Lanes [0, lanes_per_tensor) work on K and the rest on V.
 //
-// Prefill tiles: a workgroup walks BT consecutive tokens of ONE sequence, keeping the sliding
-// window in registers (each input row is loaded once and reused by the W outputs that read it).
-// A tile's W-1 row halo is the tail of the previous tile of the same sequence, or the sequence's
-// conv state / zeros for its first tile. Tiles never straddle sequences: sequence s owns logical
-// tiles [P(s), P(s) + max(1, ceil(L_s / BT))) with P(s) = floor(cu[s] / BT) + s. P is strictly
-// increasing and P(s) + max(1, ceil(L_s/BT)) <= P(s+1), so a workgroup finds its sequence by binary
-// search over cu_seqlens with no host-side scan; at most one logical tile per sequence is empty.
+// Prefill tiles: a workgroup covers one 64-lane (1 KiB) column slice of the K|V rows over a tile of
+// 4 * BT consecutive tokens of ONE sequence; each of its 4 wavefronts walks BT of those tokens,
+// keeping the sliding window in registers (each input row is loaded once and reused by the W
+// outputs that read it). Wave w > 0 gets its W-1 halo rows from wave w-1 through LDS (an
+// LDS-staged halo, so a row is fetched from HBM once); wave 0 reads the tail of the previous tile
+// of the same sequence, or the sequence's conv state / zeros for its first tile. All 4 waves use
+// the same taps and gamma, so 3 of 4 parameter loads hit in L1. Tiles never straddle sequences:
+// sequence s owns tiles [P(s), P(s) + max(1, ceil(L_s / (4*BT)))) with P(s) = floor(cu[s] /
+// (4*BT)) + s. P is strictly increasing and P(s) + max(1, ceil(L_s/(4*BT))) <= P(s+1), so a
+// workgroup finds its sequence by a wave-parallel search over cu_seqlens (one vector load per 64x
+// narrowing) with no host-side scan; at most one tile per sequence is empty. Loads are issued in
+// the order their data is needed, since vector loads return in order: taps and gamma, halo, the
+// rows the next wave needs, then the other rows.
 //
-// Conv-state ownership: only the first tile of a sequence reads the old state (its halo), so that
-// tile also writes the new state (the sequence's last W-1 raw rows, taken from the read-only input
-// and, when the sequence is shorter than W-1, from the surviving old rows). No other workgroup
-// touches that state row, so no grid-wide synchronization is needed.
-//
-// XCD-aware order: the chip hands consecutive workgroup ids to its 8 XCDs in turn, and each XCD
-// has its own L2. Logical tiles are remapped so that every XCD processes one contiguous run of
-// tiles; a tile's halo rows were then just loaded by its neighbour on the same XCD and are served
-// from that L2 instead of HBM.
+// Conv-state ownership: only the first wave of a sequence's first tile reads the old state (its
+// halo), so that wave also writes the new state (the sequence's last W-1 raw rows, taken from the
+// read-only input and, when the sequence is shorter than W-1, from the surviving old rows). No
+// other workgroup touches that state row, so no grid-wide synchronization is needed.
 //
 // Numerics (shared by prefill and decode through fused_row, so the two are bit-identical):
 // inputs widen exactly to fp32; c = taps[0]*x[0], then fma over k = 1..W-1; the sum of squares is an
@@ -44,11 +45,13 @@ namespace sc {
 namespace {
 
 constexpr int kBlock = 256;  // threads per workgroup (4 wavefronts)
-constexpr int kXcds = 8;
 
 // Build-time tuning knobs (defaults chosen by measurement on MI355X).
 #ifndef SC_PREFILL_TILE
-#define SC_PREFILL_TILE 16       // tokens per prefill tile
+#define SC_PREFILL_TILE 16       // tokens per wave span in prefill, width <= 4
+#endif
+#ifndef SC_PREFILL_TILE_WIDE
+#define SC_PREFILL_TILE_WIDE 16  // tokens per wave span in prefill, width > 4
 #endif
 #ifndef SC_PREFILL_MIN_WAVES
 #define SC_PREFILL_MIN_WAVES 2   // minimum resident waves per SIMD the register budget must allow
@@ -217,42 +220,31 @@ __device__ inline int32_t clamp_tok(int32_t v, int64_t T) {
 // ------------------------------------------------------------------------------------------------
 // Prefill
 // ------------------------------------------------------------------------------------------------
-template <int BT>
+template <int BB>
 __device__ inline int64_t tile_base(const int32_t* cu, int s, int64_t T) {
-    return (int64_t)(clamp_tok(cu[s], T) / BT) + s;
+    return (int64_t)(clamp_tok(cu[s], T) / BB) + s;
 }
 
-// Process n (<= BT) tokens starting at t0 with the window rows win[0..W-2] already in place.
-// xb: byte address of token t0's row (wave-uniform); lane_off: this lane's byte offset in a row.
-template <class E, int D, int W, int BT, bool FULL>
-__device__ inline void prefill_tokens(const StepArgs& a, const LaneParams<E, W>& p,
-                                      float (&win)[W][E::VEC], const char* xb,
-                                      int64_t stride_bytes, char* cache, int64_t row_bytes,
-                                      uint32_t lane_off, int64_t t0, int n) {
-    constexpr int LPH = D / E::VEC;
-    uint4 raw[BT];
-    int64_t slot[BT];
-    // Issue every load of the tile before any arithmetic: BT independent 16-byte loads in flight
-    // per lane, plus the tile's slot indices through the scalar cache.
-#pragma unroll
-    for (int i = 0; i < BT; ++i)
-        if (FULL || i < n) raw[i] = ldrow(xb + i * stride_bytes, lane_off);
-#pragma unroll
-    for (int i = 0; i < BT; ++i)
-        if (FULL || i < n) slot[i] = a.slot[t0 + i];
-    const float inv_d = 1.0f / (float)D;
-#pragma unroll
-    for (int i = 0; i < BT; ++i) {
-        if (FULL || i < n) {
-            E::widen(raw[i], win[W - 1]);
-            const uint4 out = fused_row<E, W, LPH>(win, p, a.eps, inv_d);
-            if (slot[i] >= 0 && slot[i] < a.num_slots) strow(cache + slot[i] * row_bytes, lane_off, out);
-#pragma unroll
-            for (int k = 0; k + 1 < W; ++k)
-#pragma unroll
-                for (int v = 0; v < E::VEC; ++v) win[k][v] = win[k + 1][v];
-        }
+// The largest s in [0, n) with P(s) <= tile, P(s) = floor(cu[s] / BB) + s (strictly increasing).
+// Wave-parallel: each round the 64 lanes test 64 evenly spaced candidates with one vector load and
+// a ballot narrows the range 64-fold, so n <= 64 costs one memory round trip and n <= 4096 two,
+// where a binary search would chain log2(n) dependent loads. Must be called by whole waves.
+template <int BB>
+__device__ inline int find_tile_seq(const int32_t* cu, int n, int64_t T, int64_t tile) {
+    const int wl = threadIdx.x & 63;
+    int base = 0, count = n;
+    while (count > 1) {
+        const int step = (count + 63) / 64;
+        const int cand = base + wl * step;
+        const bool ok = wl * step < count && tile_base<BB>(cu, cand, T) <= tile;
+        const uint64_t mask = __ballot(ok);
+        // P(base) <= tile always holds for a tile that belongs to some sequence; the prefix of
+        // set bits ends at the last candidate that still starts at or before the tile.
+        const int last = mask ? 63 - __builtin_clzll(mask) : 0;
+        base += last * step;
+        count = step < count - last * step ? step : count - last * step;
     }
+    return uniform(base);
 }
 
 template <class E, int D, int W, int BT>
@@ -260,40 +252,35 @@ __global__ void __launch_bounds__(kBlock, SC_PREFILL_MIN_WAVES) prefill_kernel(S
     constexpr int VEC = E::VEC;
     constexpr int LPH = D / VEC;
     constexpr int R = W - 1;
-    // A tile's halo lies inside the previous tile of the same sequence, and the first tile holds
-    // every position that reads the old state.
-    static_assert(BT >= R, "tile must cover the conv halo");
+    constexpr int NW = kBlock / 64;  // waves per workgroup, one BT-token span each
+    constexpr int BB = NW * BT;      // tokens per workgroup tile
+    // A wave's halo is the tail of the previous wave's span, and the tile holding a sequence's
+    // first token holds every position that reads the old state.
+    static_assert(BT >= R, "a wave's span must cover the conv halo");
+    // Tail rows that wave w hands to wave w+1 (an LDS-staged halo: HBM is read once per row).
+    __shared__ uint4 handoff[NW - 1][R > 0 ? R : 1][64];
 
-    // XCD-aware remap of the hardware workgroup id (gridDim.x is a multiple of kXcds).
-    const int G = gridDim.x;
-    const int hw = blockIdx.x;
-    const int logical = (hw % kXcds) * (G / kXcds) + hw / kXcds;
-    const int tile = logical / a.lane_blocks;
-    const int lb = logical - tile * a.lane_blocks;
-    if (tile >= a.tiles) return;
-
-    const int lane = lb * kBlock + threadIdx.x;
-    if (lane >= 2 * a.lanes_per_tensor) return;
-    const int tensor = lane >= a.lanes_per_tensor;
-    const int c = lane - tensor * a.lanes_per_tensor;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wl = threadIdx.x & 63;
+    const int lane = blockIdx.y * 64 + wl;
+    const bool active = lane < 2 * a.lanes_per_tensor;  // idle lanes load lane 0's column, store nothing
+    const int ln = active ? lane : 0;
+    const int tensor = ln >= a.lanes_per_tensor;
+    const int c = ln - tensor * a.lanes_per_tensor;
     const int h = c / LPH;
     const int d0 = (c - h * LPH) * VEC;
     const int64_t T = a.tokens;
+    const int tile = blockIdx.x;
 
-    // Which sequence owns this tile: the largest s with P(s) <= tile.
-    int lo = 0, hi = a.num_seqs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (tile_base<BT>(a.cu, mid, T) <= tile) lo = mid; else hi = mid - 1;
-    }
-    const int s = uniform(lo);
+    // Which sequence owns this tile (the same answer in every wave of the block).
+    const int s = find_tile_seq<BB>(a.cu, a.num_seqs, T, tile);
     const int64_t start = uniform((int64_t)clamp_tok(a.cu[s], T));
     int64_t end = uniform((int64_t)clamp_tok(a.cu[s + 1], T));
     if (end < start) end = start;
     const int64_t L = end - start;
-    const int64_t j = tile - tile_base<BT>(a.cu, s, T);
-    const int64_t ntiles = L > 0 ? (L + BT - 1) / BT : 1;
-    if (j < 0 || j >= ntiles) return;
+    const int64_t j = tile - tile_base<BB>(a.cu, s, T);
+    const int64_t ntiles = L > 0 ? (L + BB - 1) / BB : 1;
+    if (j < 0 || j >= ntiles) return;  // the whole workgroup leaves together
 
     const char* x = static_cast<const char*>(a.x[tensor]);
     const int64_t stride_bytes = a.x_stride[tensor] * E::BYTES;
@@ -302,11 +289,19 @@ __global__ void __launch_bounds__(kBlock, SC_PREFILL_MIN_WAVES) prefill_kernel(S
     const int64_t row_bytes = (int64_t)a.heads * D * E::BYTES;
     const uint32_t lane_off = (uint32_t)(((int64_t)h * D + d0) * E::BYTES);
 
+    // This wave's span: tokens [t0, t0 + n) of the sequence.
+    const int64_t t0 = start + j * BB + (int64_t)w * BT;
+    const int64_t rem = end - t0;
+    const int n = rem <= 0 ? 0 : (rem < BT ? (int)rem : BT);
+    const char* xb = x + t0 * stride_bytes;
+
+    // Loads in the order their data is needed (vector loads return in order): taps and gamma
+    // (cache hits), the first wave's halo, then the rows.
     LaneParams<E, W> p;
     load_params<E, W>(a.taps[tensor], a.gamma[tensor], a.heads, D, h, d0, p);
 
-    // Window rows before the tile's first token.
-    float win[W][VEC];
+    // The first wave of a tile reads its halo itself: the previous tile's last rows, or (for the
+    // sequence's first tile) the stored state or zeros.
     int32_t idx = -1;
     bool slot_ok = false, read_state = false;
     if (j == 0) {
@@ -314,30 +309,70 @@ __global__ void __launch_bounds__(kBlock, SC_PREFILL_MIN_WAVES) prefill_kernel(S
         slot_ok = R > 0 && state != nullptr && idx >= 0 && idx < a.num_state_slots;
         read_state = slot_ok && (a.has_init ? a.has_init[s] != 0 : true);
     }
-    const int64_t t0 = start + j * BT;
     const char* state_row = state + (int64_t)idx * R * row_bytes;  // used only when slot_ok
+    uint4 halo[R > 0 ? R : 1];
+    if (w == 0) {
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-        uint4 r = make_uint4(0, 0, 0, 0);
-        if (j > 0)
-            r = ldrow(x + (t0 - R + k) * stride_bytes, lane_off);
-        else if (read_state)
-            r = ldrow(state_row + k * row_bytes, lane_off);
-        E::widen(r, win[k]);
+        for (int k = 0; k < R; ++k) {
+            halo[k] = make_uint4(0, 0, 0, 0);
+            if (j > 0)
+                halo[k] = ldrow(x + (t0 - R + k) * stride_bytes, lane_off);
+            else if (read_state)
+                halo[k] = ldrow(state_row + k * row_bytes, lane_off);
+        }
+    }
+    // Row loads: the R rows the next wave needs go out first, so they arrive first (vector loads
+    // return in order) and the hand-off below waits for them only.
+    uint4 raw[BT];
+    int64_t slot[BT];
+    if (n == BT) {
+#pragma unroll
+        for (int i = BT - R; i < BT; ++i) raw[i] = ldrow(xb + i * stride_bytes, lane_off);
+#pragma unroll
+        for (int i = 0; i < BT - R; ++i) raw[i] = ldrow(xb + i * stride_bytes, lane_off);
+#pragma unroll
+        for (int i = 0; i < BT; ++i) slot[i] = a.slot[t0 + i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < BT; ++i) {
+            raw[i] = i < n ? ldrow(xb + i * stride_bytes, lane_off) : make_uint4(0, 0, 0, 0);
+            slot[i] = i < n ? a.slot[t0 + i] : -1;
+        }
+    }
+    if (R > 0) {
+        if (w + 1 < NW && n == BT) {
+#pragma unroll
+            for (int k = 0; k < R; ++k) handoff[w][k][wl] = raw[BT - R + k];
+        }
+        __syncthreads();
+        if (w > 0) {
+#pragma unroll
+            for (int k = 0; k < R; ++k) halo[k] = handoff[w - 1][k][wl];
+        }
     }
 
-    const int n = (int)((L - j * BT) < BT ? (L - j * BT) : BT);
-    if (n == BT)
-        prefill_tokens<E, D, W, BT, true>(a, p, win, x + t0 * stride_bytes, stride_bytes, cache,
-                                          row_bytes, lane_off, t0, n);
-    else if (n > 0)
-        prefill_tokens<E, D, W, BT, false>(a, p, win, x + t0 * stride_bytes, stride_bytes, cache,
-                                           row_bytes, lane_off, t0, n);
+    float win[W][VEC];
+#pragma unroll
+    for (int k = 0; k < R; ++k) E::widen(halo[k], win[k]);
+    const float inv_d = 1.0f / (float)D;
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+        if (i < n) {
+            E::widen(raw[i], win[R]);
+            const uint4 out = fused_row<E, W, LPH>(win, p, a.eps, inv_d);
+            if (active && slot[i] >= 0 && slot[i] < a.num_slots)
+                strow(cache + slot[i] * row_bytes, lane_off, out);
+#pragma unroll
+            for (int k = 0; k < R; ++k)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) win[k][v] = win[k + 1][v];
+        }
+    }
 
-    // The first tile of the sequence writes its new state: row i = e[L + i] where e is the
-    // initial window followed by the sequence's rows. Rows are written in increasing i and row i
-    // may read old row L + i > i, which is therefore still unmodified.
-    if (R > 0 && j == 0 && slot_ok) {
+    // The sequence's first tile writes its new state (its first wave read the old one): row i =
+    // e[L + i], e being the initial window followed by the sequence's rows. Rows are written in
+    // increasing i and row i may read old row L + i > i, which is therefore still unmodified.
+    if (R > 0 && j == 0 && w == 0 && slot_ok) {
         char* dst = state + (int64_t)idx * R * row_bytes;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
@@ -347,7 +382,7 @@ __global__ void __launch_bounds__(kBlock, SC_PREFILL_MIN_WAVES) prefill_kernel(S
                 r = ldrow(x + (start + e - R) * stride_bytes, lane_off);
             else if (read_state)
                 r = ldrow(dst + e * row_bytes, lane_off);
-            if (e != i || !read_state)  // e == i with a read state is a no-op copy
+            if (active && (e != i || !read_state))  // e == i with a read state is a no-op copy
                 strow(dst + i * row_bytes, lane_off, r);
         }
     }
@@ -404,11 +439,11 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(StepArgs a) {
 // ------------------------------------------------------------------------------------------------
 using KernelFn = void (*)(StepArgs);
 
-template <class E>
-constexpr int tile_tokens() { return SC_PREFILL_TILE; }
+template <int W>
+constexpr int tile_tokens() { return W <= 4 ? SC_PREFILL_TILE : SC_PREFILL_TILE_WIDE; }
 
 template <class E, int D, int W>
-constexpr KernelFn prefill_fn() { return prefill_kernel<E, D, W, tile_tokens<E>()>; }
+constexpr KernelFn prefill_fn() { return prefill_kernel<E, D, W, tile_tokens<W>()>; }
 template <class E, int D, int W>
 constexpr KernelFn decode_fn() { return decode_kernel<E, D, W>; }
 
@@ -428,17 +463,15 @@ int d_index(int D) { return D == 64 ? 0 : (D == 128 ? 1 : 2); }
 
 }  // namespace
 
-int prefill_tile_tokens(int dtype, int, int) {
-    return dtype == 0 ? tile_tokens<F32>() : tile_tokens<BF16>();
+int prefill_tile_tokens(int, int, int width) {
+    return (kBlock / 64) * (width <= 4 ? tile_tokens<1>() : tile_tokens<8>());
 }
 
 hipError_t launch_prefill(StepArgs a, int dtype, int head_dim, int width, hipStream_t stream) {
-    const int64_t lanes = 2 * (int64_t)a.lanes_per_tensor;
-    const int block = lanes >= kBlock ? kBlock : (int)((lanes + 63) / 64 * 64);
-    const int64_t total = (int64_t)a.tiles * a.lane_blocks;
-    const int64_t grid = (total + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL(kPrefill[dtype][d_index(head_dim)][width - 1], dim3((unsigned)grid),
-                       dim3(block), 0, stream, a);
+    // x: workgroup tiles of 4 * tile_tokens tokens; y: 64-lane (1 KiB) column slices of K|V rows.
+    const unsigned slices = (unsigned)((2 * (int64_t)a.lanes_per_tensor + 63) / 64);
+    hipLaunchKernelGGL(kPrefill[dtype][d_index(head_dim)][width - 1], dim3((unsigned)a.tiles, slices),
+                       dim3(kBlock), 0, stream, a);
     return hipGetLastError();
 }
 

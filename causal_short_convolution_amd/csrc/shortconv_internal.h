@@ -39,7 +39,7 @@ struct Launch {
 hipError_t launch_prefill(StepArgs a, int dtype, int head_dim, int width, hipStream_t stream);
 hipError_t launch_decode(StepArgs a, int dtype, int head_dim, int width, hipStream_t stream);
 
-// Tokens per prefill tile for a (dtype, head_dim, width) combination.
+// Tokens per prefill workgroup tile for a (dtype, head_dim, width) combination.
 int prefill_tile_tokens(int dtype, int head_dim, int width);
 
 }  // namespace sc
