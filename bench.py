@@ -83,7 +83,7 @@ def parse():
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a graph")
     ap.add_argument("--calibrate-copy", action="store_true")
-    ap.add_argument("--summarize-profile", default=None, metavar="DIR")
+    ap.add_argument("--summarize-profile", default=None, nargs="+", metavar="DIR")
     return ap.parse_args()
 
 
@@ -210,6 +210,34 @@ def measure(torch, w, steps, warmup, reseed=None, graph=True):
     }
 
 
+def copy_ceiling(torch, bytes_moved, steps, warmup):
+    """Same-bytes ceiling: a plain non-temporal copy that reads bytes_moved/2 and writes
+    bytes_moved/2, in the same rotating-replica regime and graph replay as the fused kernel."""
+    import ctypes
+    from causal_short_convolution_amd import build as hip_build
+    lib = ctypes.CDLL(hip_build.PROBE_LIB)
+    lib.sc_probe_copy.restype = ctypes.c_int
+    lib.sc_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                  ctypes.c_void_p]
+    half = (bytes_moved // 2) // 16 * 16
+    n_rep = max(2, math.ceil(2 * MALL_BYTES / (2 * half)) + 1)
+    bufs = [(torch.empty(half, dtype=torch.uint8, device="cuda:0"),
+             torch.empty(half, dtype=torch.uint8, device="cuda:0")) for _ in range(n_rep)]
+
+    def fn(src, dst):
+        def go():
+            rc = lib.sc_probe_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                   half, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"sc_probe_copy failed: {rc}")
+        return go
+
+    wall, dev_ms = time_steps(torch, [fn(a, b) for a, b in bufs], steps, warmup, graph=True)
+    per_ms = dev_ms / steps
+    return {"bytes_moved": 2 * half, "kernel_us_mean": 1e3 * per_ms,
+            "GBps": 2 * half / (per_ms * 1e-3) / 1e9}
+
+
 def calibration_copy(torch):
     n = COPY_BYTES // 2
     src = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").normal_()
@@ -252,28 +280,48 @@ def cpu_baseline(w, budget_s):
 # ------------------------------------------------------------------------------------------------
 # Profile summaries (rocprofv3 CSV output -> a short text summary for profiles/)
 # ------------------------------------------------------------------------------------------------
-def summarize_profile(d):
+def summarize_profile(dirs):
+    """Summarize rocprofv3 CSV output: kernel-trace statistics, and per-dispatch HBM traffic of
+    the fused kernels from FETCH_SIZE / WRITE_SIZE passes, each scaled by what the same counter
+    reads for the calibration copy (--calibrate-copy: COPY_BYTES read and COPY_BYTES written)."""
     import csv
     out = []
-    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
-    for path in stats:
-        out.append(f"kernel stats: {os.path.relpath(path, d)}")
-        with open(path) as f:
-            for row in csv.DictReader(f):
-                out.append(f"  {row.get('Name', '?')[:90]:90s} calls={row.get('Calls')} "
-                           f"avg_ns={float(row.get('AverageNs', 'nan')):.0f} "
-                           f"min_ns={row.get('MinNs')} max_ns={row.get('MaxNs')}")
-    ctrs = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
-    for path in ctrs:
-        agg = {}
-        with open(path) as f:
-            for row in csv.DictReader(f):
-                key = (row.get("Kernel_Name", "?"), row.get("Counter_Name", "?"))
-                agg.setdefault(key, []).append(float(row.get("Counter_Value", "nan")))
-        out.append(f"counters: {os.path.relpath(path, d)}")
-        for (k, c), vals in sorted(agg.items()):
-            out.append(f"  {k[:90]:90s} {c}: dispatch-rows={len(vals)} "
-                       f"mean={sum(vals) / len(vals):.1f}")
+    per = {}  # (kernel, counter) -> values per dispatch
+    for d in dirs:
+        for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+            out.append(f"kernel stats ({os.path.relpath(path, ROOT)}):")
+            with open(path) as f:
+                for row in csv.DictReader(f):
+                    out.append(f"  {row['Name'][:100]:100s} calls={row['Calls']:>5s} "
+                               f"avg_ns={float(row['AverageNs']):10.1f} "
+                               f"min_ns={row['MinNs']:>8s} max_ns={row['MaxNs']:>8s}")
+        for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"),
+                                     recursive=True)):
+            with open(path) as f:
+                for row in csv.DictReader(f):
+                    name = row["Kernel_Name"]
+                    kind = ("prefill_kernel" if "prefill_kernel" in name else
+                            "decode_kernel" if "decode_kernel" in name else
+                            "copy" if "copyBuffer" in name else None)
+                    if kind:
+                        per.setdefault((kind, row["Counter_Name"]), []).append(
+                            float(row["Counter_Value"]))
+    known_kib = COPY_BYTES / 1024.0
+    factors = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        copies = sorted(per.get(("copy", ctr), []))[-5:]  # the calibration copies are the largest
+        if copies:
+            factors[ctr] = known_kib / (sum(copies) / len(copies))
+            out.append(f"calibration copy {ctr}: {sum(copies) / len(copies):.1f} KiB per dispatch "
+                       f"for {known_kib:.0f} KiB moved -> factor {factors[ctr]:.4f}")
+    for kind in ("prefill_kernel", "decode_kernel"):
+        vals = {c: per.get((kind, c)) for c in ("FETCH_SIZE", "WRITE_SIZE")}
+        if all(vals.values()) and len(factors) == 2:
+            f_kib = sum(vals["FETCH_SIZE"]) / len(vals["FETCH_SIZE"])
+            w_kib = sum(vals["WRITE_SIZE"]) / len(vals["WRITE_SIZE"])
+            tr = 1024.0 * (f_kib * factors["FETCH_SIZE"] + w_kib * factors["WRITE_SIZE"])
+            out.append(f"{kind}: FETCH_SIZE {f_kib:.1f} KiB, WRITE_SIZE {w_kib:.1f} KiB per "
+                       f"dispatch -> {tr:.0f} HBM bytes per launch (calibrated)")
     print("\n".join(out))
 
 
@@ -315,6 +363,7 @@ def main():
                            "frac_of_hbm_peak": dm["achieved_GBps"] / HBM_PEAK_GBPS}
     if args.calibrate_copy:
         calibration_copy(torch)
+    ceil = copy_ceiling(torch, main_m["algorithmic_bytes"], args.steps, args.warmup)
 
     traffic = None
     if os.path.exists(TRAFFIC_SUMMARY) and args.workload == "varlen_prefill":
@@ -350,6 +399,11 @@ def main():
                      "algorithmic_bytes_per_launch": main_m["algorithmic_bytes"],
                      "kernel_us_mean": main_m["kernel_us_mean"],
                      "launch": main_m["launch"]},
+        "copy_ceiling": {"what": "non-temporal 16 B/lane copy of the same bytes, same replica "
+                                 "rotation and graph replay",
+                         "bytes_moved": ceil["bytes_moved"], "GBps": ceil["GBps"],
+                         "frac_of_peak": ceil["GBps"] / HBM_PEAK_GBPS,
+                         "kernel_over_copy": main_m["achieved_GBps"] / ceil["GBps"]},
         **extra,
     }
     if not args.no_cpu_baseline:

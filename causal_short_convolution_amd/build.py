@@ -15,6 +15,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libshortconv.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("kernels.hip", "abi.hip")]
+# measurement companion used by bench.py (same-bytes copy ceiling); not part of the C ABI
+PROBE_LIB = os.path.join(HERE, "libscprobe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "copy_probe.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -24,9 +27,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, save_temps: str = None) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, *SOURCES]
+def _hipcc(out, sources, verbose, save_temps=None):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, *sources]
     cwd = None
     if save_temps:
         os.makedirs(save_temps, exist_ok=True)
@@ -35,7 +38,12 @@ def build(verbose: bool = False, save_temps: str = None) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True, cwd=cwd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, save_temps: str = None) -> str:
+    _hipcc(LIB, SOURCES, verbose, save_temps)
+    _hipcc(PROBE_LIB, PROBE_SOURCES, verbose)
     return LIB
 
 
