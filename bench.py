@@ -91,10 +91,10 @@ def parse():
 # Device side
 # ------------------------------------------------------------------------------------------------
 def device_replicas(w, torch, n_rep, reseed=None):
-    """n_rep device copies of workload w's single step (fresh buffers each); for decode the slot
-    mappings differ between replicas (drawn with other seeds) so writes never revisit a row."""
+    """n_rep device copies of workload w (fresh buffers each). Replica r > 0 of a workload with
+    decode steps is drawn again with another seed (reseed(r)), so its decode slots differ and
+    writes never revisit a row; decode steps of all replicas share one cache pool."""
     import numpy as np
-    import workloads
     from causal_short_convolution_amd import _binding  # noqa: F401  (fails loudly if not built)
 
     dev = "cuda:0"
@@ -108,50 +108,57 @@ def device_replicas(w, torch, n_rep, reseed=None):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     shared = dict(k_taps=t(w.k_taps), v_taps=t(w.v_taps), k_gamma=t(w.k_gamma),
-                  v_gamma=t(w.v_gamma))
+                  v_gamma=t(w.v_gamma), eps=w.eps)
+    has_decode = any(st.kind == "decode" for st in w.steps)
     reps = []
-    st0 = w.steps[0]
     for r in range(n_rep):
-        st = st0
-        num_slots = w.num_slots
-        if reseed is not None and r > 0:
-            w2 = reseed(r)
-            st, num_slots = w2.steps[0], w2.num_slots
-        d = dict(shared)
-        d["k"], d["v"] = t(st.k), t(st.v)
-        d["slot"] = t(st.slot_mapping.astype(np.int64))
-        d["sidx"] = t(st.state_idx.astype(np.int32))
-        if st.kind == "prefill":
-            d["cu"] = t(st.cu_seqlens.astype(np.int32))
-            d["hinit"] = t(st.has_init.astype(np.uint8))
-        d["k_state"], d["v_state"] = t(w.k_state), t(w.v_state)
-        d["num_slots"] = num_slots
-        reps.append(d)
-    # caches: prefill replicas each get their own; decode replicas share one pool large enough
-    # for every replica's slots (distinct random slots, so rows are not revisited)
-    if st0.kind == "prefill":
-        for d in reps:
-            d["k_cache"] = torch.empty((d["num_slots"], w.H, w.D), dtype=dt, device=dev)
-            d["v_cache"] = torch.empty((d["num_slots"], w.H, w.D), dtype=dt, device=dev)
-    else:
-        ns = max(d["num_slots"] for d in reps)
+        wr = reseed(r) if (reseed is not None and r > 0) else w
+        steps = []
+        for st in wr.steps:
+            d = dict(shared, kind=st.kind)
+            d["k"], d["v"] = t(st.k), t(st.v)
+            d["slot"] = t(st.slot_mapping.astype(np.int64))
+            d["sidx"] = t(st.state_idx.astype(np.int32))
+            if st.kind == "prefill":
+                d["cu"] = t(st.cu_seqlens.astype(np.int32))
+                d["hinit"] = t(st.has_init.astype(np.uint8))
+            steps.append(d)
+        rep = {"steps": steps, "num_slots": wr.num_slots,
+               "k_state": t(wr.k_state), "v_state": t(wr.v_state)}
+        reps.append(rep)
+    if has_decode:  # one pool large enough for every replica's slots
+        ns = max(r["num_slots"] for r in reps)
         kc = torch.empty((ns, w.H, w.D), dtype=dt, device=dev)
         vc = torch.empty((ns, w.H, w.D), dtype=dt, device=dev)
-        for d in reps:
-            d["k_cache"], d["v_cache"] = kc, vc
+        for r in reps:
+            r["k_cache"], r["v_cache"] = kc, vc
+    else:
+        for r in reps:
+            r["k_cache"] = torch.empty((r["num_slots"], w.H, w.D), dtype=dt, device=dev)
+            r["v_cache"] = torch.empty((r["num_slots"], w.H, w.D), dtype=dt, device=dev)
     return reps
 
 
-def launcher(w, d):
+def launcher(w, rep):
+    """One bench step: every call of the workload, in order, on the current stream."""
     from causal_short_convolution_amd import shortconv_kv_decode, shortconv_kv_prefill
-    if "cu" in d:
-        return lambda: shortconv_kv_prefill(
-            d["k"], d["v"], d["cu"], d["k_taps"], d["v_taps"], d["k_gamma"], d["v_gamma"], w.eps,
-            d["k_state"], d["v_state"], d["sidx"], d["hinit"], d["slot"], d["k_cache"],
-            d["v_cache"])
-    return lambda: shortconv_kv_decode(
-        d["k"], d["v"], d["k_taps"], d["v_taps"], d["k_gamma"], d["v_gamma"], w.eps, d["k_state"],
-        d["v_state"], d["sidx"], d["slot"], d["k_cache"], d["v_cache"])
+    calls = []
+    for d in rep["steps"]:
+        if d["kind"] == "prefill":
+            calls.append(lambda d=d: shortconv_kv_prefill(
+                d["k"], d["v"], d["cu"], d["k_taps"], d["v_taps"], d["k_gamma"], d["v_gamma"],
+                d["eps"], rep["k_state"], rep["v_state"], d["sidx"], d["hinit"], d["slot"],
+                rep["k_cache"], rep["v_cache"]))
+        else:
+            calls.append(lambda d=d: shortconv_kv_decode(
+                d["k"], d["v"], d["k_taps"], d["v_taps"], d["k_gamma"], d["v_gamma"], d["eps"],
+                rep["k_state"], rep["v_state"], d["sidx"], d["slot"], rep["k_cache"],
+                rep["v_cache"]))
+
+    def step():
+        for c in calls:
+            c()
+    return step
 
 
 def time_steps(torch, fns, steps, warmup, graph=True):
@@ -190,23 +197,24 @@ def time_steps(torch, fns, steps, warmup, graph=True):
 
 
 def measure(torch, w, steps, warmup, reseed=None, graph=True):
-    step = w.steps[0]
-    alg = algorithmic_bytes(w, step)
+    alg = sum(algorithmic_bytes(w, st) for st in w.steps)
+    tokens = w.tokens
     n_rep = max(2, math.ceil(2 * MALL_BYTES / alg) + 1)
     reps = device_replicas(w, torch, n_rep, reseed)
-    fns = [launcher(w, d) for d in reps]
+    fns = [launcher(w, r) for r in reps]
     wall, dev_ms = time_steps(torch, fns, steps, warmup, graph)
-    per_launch_ms = dev_ms / steps
+    per_step_ms = dev_ms / steps
     return {
-        "tokens_per_step": step.tokens,
+        "tokens_per_step": tokens,
+        "launches_per_step": len(w.steps),
         "replicas": n_rep,
         "launch": "hip graph replay" if graph else "eager",
         "wall_s": wall,
         "ms_per_step": 1e3 * wall / steps,
-        "tokens_per_s": step.tokens * steps / wall,
-        "kernel_us_mean": 1e3 * per_launch_ms,
+        "tokens_per_s": tokens * steps / wall,
+        "kernel_us_mean": 1e3 * per_step_ms,
         "algorithmic_bytes": alg,
-        "achieved_GBps": alg / (per_launch_ms * 1e-3) / 1e9,
+        "achieved_GBps": alg / (per_step_ms * 1e-3) / 1e9,
     }
 
 
@@ -251,28 +259,32 @@ def calibration_copy(torch):
 # CPU baseline: the fp64 oracle, as it stands, on the same workload
 # ------------------------------------------------------------------------------------------------
 def cpu_baseline(w, budget_s):
+    """The oracle on the whole workload (every call, the state pools carried from call to call),
+    repeated until about budget_s seconds of CPU time have been spent."""
     import oracle
     threads = max(1, min(16, os.cpu_count() or 1))
-    st = w.steps[0]
     reps = 0
     c0, t0 = time.process_time(), time.perf_counter()
     while True:
-        if st.kind == "prefill":
-            oracle.fused_prefill(st.k, st.v, st.cu_seqlens, w.k_taps, w.v_taps, w.k_gamma,
-                                 w.v_gamma, w.eps, w.k_state, w.v_state, st.state_idx,
-                                 st.has_init, st.slot_mapping, w.num_slots, cond=False,
-                                 nthreads=threads)
-        else:
-            oracle.fused_decode(st.k, st.v, w.k_taps, w.v_taps, w.k_gamma, w.v_gamma, w.eps,
-                                w.k_state, w.v_state, st.state_idx, st.slot_mapping, w.num_slots,
-                                cond=False, nthreads=threads)
+        ks, vs = w.k_state, w.v_state
+        for st in w.steps:
+            if st.kind == "prefill":
+                r = oracle.fused_prefill(st.k, st.v, st.cu_seqlens, w.k_taps, w.v_taps, w.k_gamma,
+                                         w.v_gamma, w.eps, ks, vs, st.state_idx, st.has_init,
+                                         st.slot_mapping, w.num_slots, cond=False,
+                                         nthreads=threads)
+            else:
+                r = oracle.fused_decode(st.k, st.v, w.k_taps, w.v_taps, w.k_gamma, w.v_gamma,
+                                        w.eps, ks, vs, st.state_idx, st.slot_mapping,
+                                        w.num_slots, cond=False, nthreads=threads)
+            ks, vs = r.k_state, r.v_state
         reps += 1
         if time.process_time() - c0 >= budget_s:
             break
     wall = time.perf_counter() - t0
-    return {"value": st.tokens * reps / wall, "unit": "tokens/s", "cores": threads,
+    return {"value": w.tokens * reps / wall, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"the whole {w.name} workload ({st.tokens} tokens, K and V, fp64) "
+            "sample": f"the whole {w.name} workload ({w.tokens} tokens, K and V, fp64) "
                       f"repeated {reps}x: {wall:.1f} s wall, "
                       f"{time.process_time() - c0:.1f} s CPU on {threads} threads"}
 
@@ -348,11 +360,10 @@ def main():
 
     n = WORKLOADS[args.workload]
     w = workloads.config(n, seed=args.seed)
-    if len(w.steps) != 1:
-        raise SystemExit("bench.py: the mixed workload is measured by its two steps separately")
+    has_decode = any(st.kind == "decode" for st in w.steps)
     main_m = measure(torch, w, args.steps, args.warmup,
                      reseed=(lambda r: workloads.config(n, seed=args.seed + 1000 * r))
-                     if w.steps[0].kind == "decode" else None, graph=not args.eager)
+                     if has_decode else None, graph=not args.eager)
     extra = {}
     if not args.no_decode and args.workload != "decode":
         wd = workloads.config(3, seed=args.seed)
@@ -374,7 +385,6 @@ def main():
         if kv.get("kernel_source_sha256") == kernel_source_sha():
             traffic = float(kv["hbm_bytes_per_launch"])
 
-    st = w.steps[0]
     line = {
         "metric": METRIC,
         "value": main_m["tokens_per_s"],
@@ -389,13 +399,14 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "recipe": w.recipe, "seed": args.seed,
-                   "tokens_per_step": st.tokens, "seqs": st.num_seqs, "heads": w.H,
+                   "tokens_per_step": w.tokens, "launches_per_step": len(w.steps),
+                   "seqs": sum(x.num_seqs for x in w.steps), "heads": w.H,
                    "head_dim": w.D, "width": w.W, "io": w.dtype, "block_size": w.block_size,
                    "replicas": main_m["replicas"], "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": main_m["achieved_GBps"], "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": main_m["achieved_GBps"] / HBM_PEAK_GBPS,
                      "traffic": traffic,
-                     "kernel": "prefill_kernel" if st.kind == "prefill" else "decode_kernel",
+                     "kernel": "+".join(f"{x.kind}_kernel" for x in w.steps),
                      "algorithmic_bytes_per_launch": main_m["algorithmic_bytes"],
                      "kernel_us_mean": main_m["kernel_us_mean"],
                      "launch": main_m["launch"]},

@@ -123,7 +123,7 @@ SC_API int shortconv_kv_prefill(const void* k, const void* v, int64_t k_tok_stri
     a.num_seqs = num_seqs;
     const int bt = sc::prefill_tile_tokens(dtype, head_dim, width);
     const int64_t tiles = total_tokens / bt + num_seqs;  // upper bound, see kernels.hip
-    if (tiles > INT32_MAX || (2 * (int64_t)a.lanes_per_tensor + 63) / 64 > 65535)
+    if (tiles * ((2 * (int64_t)a.lanes_per_tensor + 63) / 64) > INT32_MAX)
         return fail(SC_ERR_UNSUPPORTED, "%s: problem too large for one launch", fn);
     a.tiles = (int32_t)tiles;
     hipError_t e = sc::launch_prefill(a, dtype, head_dim, width, (hipStream_t)stream);

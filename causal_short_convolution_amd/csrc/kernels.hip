@@ -262,7 +262,12 @@ __global__ void __launch_bounds__(kBlock, SC_PREFILL_MIN_WAVES) prefill_kernel(S
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wl = threadIdx.x & 63;
-    const int lane = blockIdx.y * 64 + wl;
+    // Linear workgroup id = tile * slices + slice: the slices of one tile (the 1 KiB pieces of the
+    // same rows) are dispatched together, so each row is read and written in one burst.
+    const int slices = a.lane_blocks;
+    const int tile = blockIdx.x / slices;
+    const int slice = blockIdx.x - tile * slices;
+    const int lane = slice * 64 + wl;
     const bool active = lane < 2 * a.lanes_per_tensor;  // idle lanes load lane 0's column, store nothing
     const int ln = active ? lane : 0;
     const int tensor = ln >= a.lanes_per_tensor;
@@ -270,7 +275,6 @@ __global__ void __launch_bounds__(kBlock, SC_PREFILL_MIN_WAVES) prefill_kernel(S
     const int h = c / LPH;
     const int d0 = (c - h * LPH) * VEC;
     const int64_t T = a.tokens;
-    const int tile = blockIdx.x;
 
     // Which sequence owns this tile (the same answer in every wave of the block).
     const int s = find_tile_seq<BB>(a.cu, a.num_seqs, T, tile);
@@ -468,9 +472,11 @@ int prefill_tile_tokens(int, int, int width) {
 }
 
 hipError_t launch_prefill(StepArgs a, int dtype, int head_dim, int width, hipStream_t stream) {
-    // x: workgroup tiles of 4 * tile_tokens tokens; y: 64-lane (1 KiB) column slices of K|V rows.
-    const unsigned slices = (unsigned)((2 * (int64_t)a.lanes_per_tensor + 63) / 64);
-    hipLaunchKernelGGL(kPrefill[dtype][d_index(head_dim)][width - 1], dim3((unsigned)a.tiles, slices),
+    // One workgroup per (tile of 4 * tile_tokens tokens, 64-lane (1 KiB) column slice of the
+    // K|V rows); a.lane_blocks carries the number of slices.
+    a.lane_blocks = (int32_t)((2 * (int64_t)a.lanes_per_tensor + 63) / 64);
+    const int64_t blocks = (int64_t)a.tiles * a.lane_blocks;
+    hipLaunchKernelGGL(kPrefill[dtype][d_index(head_dim)][width - 1], dim3((unsigned)blocks),
                        dim3(kBlock), 0, stream, a);
     return hipGetLastError();
 }
