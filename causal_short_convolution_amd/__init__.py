@@ -1,11 +1,14 @@
 """Fused ShortConv K/V step for AMD Instinct MI355X (gfx950).
 
 Causal depthwise convolution over tokens of the projected K and V, per-head RMSNorm, paged
-KV-cache write and rolling conv-state update, in one HIP kernel per call. The compute lives in
-``libshortconv.so`` (C ABI, ``include/shortconv.h``); this package only marshals torch tensors.
+KV-cache write and rolling conv-state update, in one HIP kernel per call; plus speculative
+verification with per-token conv-state snapshots and the commit of an accepted prefix. The
+compute lives in ``libshortconv.so`` (C ABI, ``include/shortconv.h``); this package only
+marshals torch tensors.
 """
 from ._binding import (LIBRARY_PATH, ShortConvError, abi_version, last_error, load_library,
-                       shortconv_kv_decode, shortconv_kv_prefill)
+                       shortconv_kv_decode, shortconv_kv_prefill, shortconv_kv_verify,
+                       shortconv_state_commit)
 
 __all__ = [
     "LIBRARY_PATH",
@@ -15,4 +18,6 @@ __all__ = [
     "load_library",
     "shortconv_kv_decode",
     "shortconv_kv_prefill",
+    "shortconv_kv_verify",
+    "shortconv_state_commit",
 ]

@@ -46,6 +46,12 @@ def load_library(path: str = LIBRARY_PATH):
     lib.shortconv_kv_decode.restype = ctypes.c_int
     lib.shortconv_kv_decode.argtypes = [P, P, I64, I64, I32, P, P, P, P, F, P, P, I64, P, P, P, P,
                                         I64, I32, I32, I32, I32, P]
+    lib.shortconv_kv_verify.restype = ctypes.c_int
+    lib.shortconv_kv_verify.argtypes = [P, P, I64, I64, P, I32, I64, P, P, P, P, F, P, P, I64, P,
+                                        P, P, I32, P, P, P, I64, I32, I32, I32, I32, P]
+    lib.shortconv_state_commit.restype = ctypes.c_int
+    lib.shortconv_state_commit.argtypes = [P, P, I32, P, I64, P, I32, P, P, I64, P, I32, I32, I32,
+                                           I32, P]
     lib.shortconv_last_error.restype = ctypes.c_char_p
     lib.shortconv_last_error.argtypes = []
     lib.shortconv_abi_version.restype = ctypes.c_int
@@ -121,4 +127,43 @@ def shortconv_kv_decode(k_new, v_new, k_taps, v_taps, k_gamma, v_gamma, eps, k_s
             _ptr(k_state), _ptr(v_state), S, _ptr(state_idx), _ptr(slot_mapping), _ptr(k_cache),
             _ptr(v_cache), k_cache.shape[0], H, D, W, SC_DTYPE[k_new.dtype],
             _stream_handle(k_new.device, stream))
+    _check(rc)
+
+
+def shortconv_kv_verify(k, v, cu_seqlens, k_taps, v_taps, k_gamma, v_gamma, eps, k_state, v_state,
+                        state_idx, k_snap, v_snap, slot_mapping, k_cache, v_cache, *,
+                        stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Speculative verification (see include/shortconv.h): outputs as a prefill that resumes
+    every sequence from its stored state; pools read only; per-token states go to
+    k_snap/v_snap [N, max_tokens, W-1, H, D] (None when W == 1)."""
+    lib = load_library()
+    W, H, D = k_taps.shape
+    S = k_state.shape[0] if k_state is not None else 0
+    max_tokens = k_snap.shape[1] if k_snap is not None else 1
+    with torch.cuda.device(k.device):
+        rc = lib.shortconv_kv_verify(
+            _ptr(k), _ptr(v), _rows(k, "k"), _rows(v, "v"), _ptr(cu_seqlens),
+            cu_seqlens.shape[0] - 1, k.shape[0], _ptr(k_taps), _ptr(v_taps), _ptr(k_gamma),
+            _ptr(v_gamma), float(eps), _ptr(k_state), _ptr(v_state), S, _ptr(state_idx),
+            _ptr(k_snap), _ptr(v_snap), max_tokens, _ptr(slot_mapping), _ptr(k_cache),
+            _ptr(v_cache), k_cache.shape[0], H, D, W, SC_DTYPE[k.dtype],
+            _stream_handle(k.device, stream))
+    _check(rc)
+
+
+def shortconv_state_commit(k_snap, v_snap, cu_seqlens, total_tokens, accepted, k_state, v_state,
+                           state_idx, *, width, num_heads, head_dim,
+                           stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Install the accepted prefix's snapshot in the state pools (see include/shortconv.h)."""
+    lib = load_library()
+    S = k_state.shape[0] if k_state is not None else 0
+    max_tokens = k_snap.shape[1] if k_snap is not None else 1
+    dev = k_state.device if k_state is not None else accepted.device
+    dtype = k_state.dtype if k_state is not None else torch.bfloat16
+    with torch.cuda.device(dev):
+        rc = lib.shortconv_state_commit(
+            _ptr(k_snap), _ptr(v_snap), max_tokens, _ptr(cu_seqlens), int(total_tokens),
+            _ptr(accepted), cu_seqlens.shape[0] - 1, _ptr(k_state), _ptr(v_state), S,
+            _ptr(state_idx), num_heads, head_dim, width, SC_DTYPE[dtype],
+            _stream_handle(dev, stream))
     _check(rc)

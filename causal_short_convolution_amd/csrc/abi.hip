@@ -158,6 +158,96 @@ SC_API int shortconv_kv_decode(const void* k_new, const void* v_new, int64_t k_t
     return SC_OK;
 }
 
+SC_API int shortconv_kv_verify(const void* k, const void* v, int64_t k_tok_stride,
+                               int64_t v_tok_stride, const int32_t* cu_seqlens, int32_t num_seqs,
+                               int64_t total_tokens, const float* k_taps, const float* v_taps,
+                               const float* k_gamma, const float* v_gamma, float eps,
+                               const void* k_state, const void* v_state, int64_t num_state_slots,
+                               const int32_t* state_idx, void* k_snap, void* v_snap,
+                               int32_t max_tokens, const int64_t* slot_mapping, void* k_cache,
+                               void* v_cache, int64_t num_slots, int32_t num_heads,
+                               int32_t head_dim, int32_t width, int32_t dtype, void* stream) {
+    const char* fn = "shortconv_kv_verify";
+    g_err[0] = 0;
+    int rc = check_common(fn, k, v, k_tok_stride, v_tok_stride, k_taps, v_taps, k_gamma, v_gamma,
+                          eps, k_state, v_state, num_state_slots, slot_mapping, k_cache, v_cache,
+                          num_slots, num_heads, head_dim, width, dtype, total_tokens);
+    if (rc != SC_OK) return rc;
+    if (num_seqs < 0) return fail(SC_ERR_INVALID, "%s: num_seqs < 0", fn);
+    if (total_tokens < 0 || total_tokens > INT32_MAX)
+        return fail(SC_ERR_INVALID, "%s: total_tokens must be in [0, 2^31)", fn);
+    if (max_tokens < 1) return fail(SC_ERR_INVALID, "%s: max_tokens < 1", fn);
+    if (num_seqs == 0 || total_tokens == 0) return SC_OK;  // nothing to compute or snapshot
+    if (!cu_seqlens) return fail(SC_ERR_INVALID, "%s: null cu_seqlens", fn);
+    if (width > 1 && (!k_snap || !v_snap))
+        return fail(SC_ERR_INVALID, "%s: null snapshot buffer with width %d > 1", fn, width);
+    if (!aligned16(k_snap) || !aligned16(v_snap))
+        return fail(SC_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
+    sc::StepArgs a = make_args(k, v, k_tok_stride, v_tok_stride, k_taps, v_taps, k_gamma, v_gamma,
+                               eps, const_cast<void*>(k_state), const_cast<void*>(v_state),
+                               num_state_slots, state_idx, slot_mapping, k_cache, v_cache,
+                               num_slots, num_heads, head_dim, width, dtype);
+    a.cu = cu_seqlens;
+    a.tokens = total_tokens;
+    a.num_seqs = num_seqs;
+    if (a.lane_blocks > 65535) return fail(SC_ERR_UNSUPPORTED, "%s: num_heads too large", fn);
+    sc::VerifyArgs va = {};
+    va.snap[0] = width > 1 ? k_snap : nullptr;
+    va.snap[1] = width > 1 ? v_snap : nullptr;
+    va.max_tokens = max_tokens;
+    hipError_t e = sc::launch_verify(a, va, dtype, head_dim, width, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(SC_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return SC_OK;
+}
+
+SC_API int shortconv_state_commit(const void* k_snap, const void* v_snap, int32_t max_tokens,
+                                  const int32_t* cu_seqlens, int64_t total_tokens,
+                                  const int32_t* accepted, int32_t num_seqs, void* k_state,
+                                  void* v_state, int64_t num_state_slots,
+                                  const int32_t* state_idx, int32_t num_heads, int32_t head_dim,
+                                  int32_t width, int32_t dtype, void* stream) {
+    const char* fn = "shortconv_state_commit";
+    g_err[0] = 0;
+    if (dtype != SC_DTYPE_F32 && dtype != SC_DTYPE_BF16)
+        return fail(SC_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+        return fail(SC_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128, 256}", fn, head_dim);
+    if (width < 1 || width > 8)
+        return fail(SC_ERR_UNSUPPORTED, "%s: width %d not in [1, 8]", fn, width);
+    if (num_heads < 1) return fail(SC_ERR_INVALID, "%s: num_heads %d < 1", fn, num_heads);
+    if (num_seqs < 0 || num_state_slots < 0 || total_tokens < 0 || total_tokens > INT32_MAX)
+        return fail(SC_ERR_INVALID, "%s: negative size", fn);
+    if (max_tokens < 1) return fail(SC_ERR_INVALID, "%s: max_tokens < 1", fn);
+    if (width == 1 || num_seqs == 0 || num_state_slots == 0) return SC_OK;  // no state to install
+    if (!k_snap || !v_snap || !k_state || !v_state || !cu_seqlens || !accepted)
+        return fail(SC_ERR_INVALID, "%s: null pointer", fn);
+    const void* ptrs[] = {k_snap, v_snap, k_state, v_state};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return fail(SC_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
+    if ((int64_t)num_heads * head_dim > (int64_t)1 << 20)
+        return fail(SC_ERR_UNSUPPORTED, "%s: num_heads too large", fn);
+    sc::StepArgs a = {};
+    a.state[0] = k_state;
+    a.state[1] = v_state;
+    a.num_state_slots = num_state_slots;
+    a.state_idx = state_idx;
+    a.cu = cu_seqlens;
+    a.tokens = total_tokens;
+    a.num_seqs = num_seqs;
+    a.heads = num_heads;
+    a.lanes_per_tensor = num_heads * (head_dim / (16 / element_bytes(dtype)));
+    a.lane_blocks = (int32_t)((2 * (int64_t)a.lanes_per_tensor + 255) / 256);
+    if (a.lane_blocks > 65535) return fail(SC_ERR_UNSUPPORTED, "%s: num_heads too large", fn);
+    sc::VerifyArgs va = {};
+    va.snap[0] = const_cast<void*>(k_snap);
+    va.snap[1] = const_cast<void*>(v_snap);
+    va.accepted = accepted;
+    va.max_tokens = max_tokens;
+    hipError_t e = sc::launch_commit(a, va, dtype, head_dim, width, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(SC_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return SC_OK;
+}
+
 SC_API const char* shortconv_last_error(void) { return g_err; }
 
 SC_API int shortconv_abi_version(void) { return SHORTCONV_ABI_VERSION; }

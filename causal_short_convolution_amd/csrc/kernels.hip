@@ -439,6 +439,129 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(StepArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// Speculative verification: each sequence runs its candidate tokens from the stored conv state,
+// which it only reads; the state after every token goes to a snapshot buffer instead, so that the
+// state of any accepted prefix can be installed afterwards (commit_kernel).
+// ------------------------------------------------------------------------------------------------
+constexpr int kVerifyChunk = 16;  // tokens whose rows are loaded together per pass
+
+template <class E, int D, int W>
+__global__ void __launch_bounds__(kBlock) verify_kernel(StepArgs a, VerifyArgs va) {
+    constexpr int VEC = E::VEC;
+    constexpr int LPH = D / VEC;
+    constexpr int R = W - 1;
+    constexpr int K = kVerifyChunk;
+    const int s = blockIdx.x;
+    const int lane = blockIdx.y * kBlock + threadIdx.x;
+    if (lane >= 2 * a.lanes_per_tensor) return;
+    const int tensor = lane >= a.lanes_per_tensor;
+    const int c = lane - tensor * a.lanes_per_tensor;
+    const int h = c / LPH;
+    const int d0 = (c - h * LPH) * VEC;
+    const int64_t row_bytes = (int64_t)a.heads * D * E::BYTES;
+    const uint32_t lane_off = (uint32_t)(((int64_t)h * D + d0) * E::BYTES);
+    const char* x = static_cast<const char*>(a.x[tensor]);
+    const int64_t stride_bytes = a.x_stride[tensor] * E::BYTES;
+    char* cache = static_cast<char*>(a.cache[tensor]);
+    const char* state = static_cast<const char*>(a.state[tensor]);
+    char* snap = static_cast<char*>(va.snap[tensor]);
+
+    const int64_t T = a.tokens;
+    const int64_t start = uniform((int64_t)clamp_tok(a.cu[s], T));
+    int64_t end = uniform((int64_t)clamp_tok(a.cu[s + 1], T));
+    if (end < start) end = start;
+    const int64_t L = end - start;
+    const int32_t idx = uniform(a.state_idx ? a.state_idx[s] : s);
+    const bool slot_ok = R > 0 && state != nullptr && idx >= 0 && idx < a.num_state_slots;
+
+    LaneParams<E, W> p;
+    load_params<E, W>(a.taps[tensor], a.gamma[tensor], a.heads, D, h, d0, p);
+    // Rolling window of raw rows (for bit-exact snapshots) and its widened copy.
+    uint4 rw[R > 0 ? R : 1];
+    float win[W][VEC];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        rw[k] = slot_ok ? ldrow(state + ((int64_t)idx * R + k) * row_bytes, lane_off)
+                        : make_uint4(0, 0, 0, 0);
+        E::widen(rw[k], win[k]);
+    }
+    const float inv_d = 1.0f / (float)D;
+    char* snap_seq = snap + (int64_t)s * va.max_tokens * R * row_bytes;
+
+    for (int64_t c0 = 0; c0 < L; c0 += K) {
+        uint4 raw[K];
+        int64_t slot[K];
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+            if (c0 + i < L) {
+                raw[i] = ldrow(x + (start + c0 + i) * stride_bytes, lane_off);
+                slot[i] = a.slot[start + c0 + i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+            if (c0 + i < L) {
+                E::widen(raw[i], win[R]);
+                const uint4 out = fused_row<E, W, LPH>(win, p, a.eps, inv_d);
+                if (slot[i] >= 0 && slot[i] < a.num_slots)
+                    strow(cache + slot[i] * row_bytes, lane_off, out);
+#pragma unroll
+                for (int k = 0; k < R; ++k)
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) win[k][v] = win[k + 1][v];
+                if (R > 0) {
+#pragma unroll
+                    for (int k = 0; k + 1 < R; ++k) rw[k] = rw[k + 1];
+                    rw[R - 1] = raw[i];
+                    if (snap != nullptr && c0 + i < va.max_tokens) {
+                        char* dst = snap_seq + (c0 + i) * R * row_bytes;
+#pragma unroll
+                        for (int k = 0; k < R; ++k) strow(dst + k * row_bytes, lane_off, rw[k]);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Installs the snapshot of the accepted prefix: pool row state_idx[s] = snapshot (s, m - 1) with
+// m = min(accepted[s], L_s, max_tokens); m == 0 leaves the row as it is.
+template <class E, int D, int W>
+__global__ void __launch_bounds__(kBlock) commit_kernel(StepArgs a, VerifyArgs va) {
+    constexpr int VEC = E::VEC;
+    constexpr int LPH = D / VEC;
+    constexpr int R = W - 1;
+    const int s = blockIdx.x;
+    const int lane = blockIdx.y * kBlock + threadIdx.x;
+    if (R == 0 || lane >= 2 * a.lanes_per_tensor) return;
+    const int tensor = lane >= a.lanes_per_tensor;
+    const int c = lane - tensor * a.lanes_per_tensor;
+    const int h = c / LPH;
+    const int d0 = (c - h * LPH) * VEC;
+    const int64_t row_bytes = (int64_t)a.heads * D * E::BYTES;
+    const uint32_t lane_off = (uint32_t)(((int64_t)h * D + d0) * E::BYTES);
+    char* state = static_cast<char*>(a.state[tensor]);
+    const char* snap = static_cast<const char*>(va.snap[tensor]);
+
+    const int64_t T = a.tokens;
+    const int64_t start = (int64_t)clamp_tok(a.cu[s], T);
+    int64_t end = (int64_t)clamp_tok(a.cu[s + 1], T);
+    if (end < start) end = start;
+    int64_t m = va.accepted[s];
+    if (m > end - start) m = end - start;
+    if (m > va.max_tokens) m = va.max_tokens;
+    const int32_t idx = a.state_idx ? a.state_idx[s] : s;
+    if (m < 1 || state == nullptr || snap == nullptr || idx < 0 || idx >= a.num_state_slots) return;
+    const char* src = snap + ((int64_t)s * va.max_tokens + (m - 1)) * R * row_bytes;
+    char* dst = state + (int64_t)idx * R * row_bytes;
+    uint4 r[R > 0 ? R : 1];
+#pragma unroll
+    for (int k = 0; k < R; ++k) r[k] = ldrow(src + k * row_bytes, lane_off);
+#pragma unroll
+    for (int k = 0; k < R; ++k) strow(dst + k * row_bytes, lane_off, r[k]);
+}
+
+// ------------------------------------------------------------------------------------------------
 // Dispatch tables: [dtype][head_dim index][width - 1]
 // ------------------------------------------------------------------------------------------------
 using KernelFn = void (*)(StepArgs);
@@ -450,6 +573,11 @@ template <class E, int D, int W>
 constexpr KernelFn prefill_fn() { return prefill_kernel<E, D, W, tile_tokens<W>()>; }
 template <class E, int D, int W>
 constexpr KernelFn decode_fn() { return decode_kernel<E, D, W>; }
+using VerifyFn = void (*)(StepArgs, VerifyArgs);
+template <class E, int D, int W>
+constexpr VerifyFn verify_fn() { return verify_kernel<E, D, W>; }
+template <class E, int D, int W>
+constexpr VerifyFn commit_fn() { return commit_kernel<E, D, W>; }
 
 #define SC_ROW(KIND, E, D)                                                                   \
     { KIND##_fn<E, D, 1>(), KIND##_fn<E, D, 2>(), KIND##_fn<E, D, 3>(), KIND##_fn<E, D, 4>(), \
@@ -462,6 +590,8 @@ constexpr KernelFn decode_fn() { return decode_kernel<E, D, W>; }
 
 const KernelFn kPrefill[2][3][8] = SC_TABLE(prefill);
 const KernelFn kDecode[2][3][8] = SC_TABLE(decode);
+const VerifyFn kVerify[2][3][8] = SC_TABLE(verify);
+const VerifyFn kCommit[2][3][8] = SC_TABLE(commit);
 
 int d_index(int D) { return D == 64 ? 0 : (D == 128 ? 1 : 2); }
 
@@ -487,6 +617,26 @@ hipError_t launch_decode(StepArgs a, int dtype, int head_dim, int width, hipStre
     hipLaunchKernelGGL(kDecode[dtype][d_index(head_dim)][width - 1],
                        dim3((unsigned)a.tokens, (unsigned)a.lane_blocks), dim3(block), 0, stream,
                        a);
+    return hipGetLastError();
+}
+
+hipError_t launch_verify(StepArgs a, VerifyArgs va, int dtype, int head_dim, int width,
+                         hipStream_t stream) {
+    const int64_t lanes = 2 * (int64_t)a.lanes_per_tensor;
+    const int block = lanes >= kBlock ? kBlock : (int)((lanes + 63) / 64 * 64);
+    hipLaunchKernelGGL(kVerify[dtype][d_index(head_dim)][width - 1],
+                       dim3((unsigned)a.num_seqs, (unsigned)a.lane_blocks), dim3(block), 0, stream,
+                       a, va);
+    return hipGetLastError();
+}
+
+hipError_t launch_commit(StepArgs a, VerifyArgs va, int dtype, int head_dim, int width,
+                         hipStream_t stream) {
+    const int64_t lanes = 2 * (int64_t)a.lanes_per_tensor;
+    const int block = lanes >= kBlock ? kBlock : (int)((lanes + 63) / 64 * 64);
+    hipLaunchKernelGGL(kCommit[dtype][d_index(head_dim)][width - 1],
+                       dim3((unsigned)a.num_seqs, (unsigned)a.lane_blocks), dim3(block), 0, stream,
+                       a, va);
     return hipGetLastError();
 }
 

@@ -29,15 +29,20 @@ struct StepArgs {
     float eps;
 };
 
-// Launch geometry chosen by the kernels for a given problem.
-struct Launch {
-    dim3 grid;
-    dim3 block;
+// Extra arguments of speculative verification and of its commit.
+struct VerifyArgs {
+    void* snap[2];             // [num_seqs][max_tokens][W-1][H][D] per tensor, or null (W == 1)
+    const int32_t* accepted;   // commit only: int32 [num_seqs]
+    int32_t max_tokens;
 };
 
 // Returns hipSuccess or the launch error. `dtype`: 0 = fp32, 1 = bf16. Shapes already validated.
 hipError_t launch_prefill(StepArgs a, int dtype, int head_dim, int width, hipStream_t stream);
 hipError_t launch_decode(StepArgs a, int dtype, int head_dim, int width, hipStream_t stream);
+hipError_t launch_verify(StepArgs a, VerifyArgs va, int dtype, int head_dim, int width,
+                         hipStream_t stream);
+hipError_t launch_commit(StepArgs a, VerifyArgs va, int dtype, int head_dim, int width,
+                         hipStream_t stream);
 
 // Tokens per prefill workgroup tile for a (dtype, head_dim, width) combination.
 int prefill_tile_tokens(int dtype, int head_dim, int width);

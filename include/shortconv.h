@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SHORTCONV_ABI_VERSION 1
+#define SHORTCONV_ABI_VERSION 2
 
 typedef enum {
     SC_DTYPE_F32 = 0,  /* IEEE binary32 */
@@ -119,6 +119,47 @@ int shortconv_kv_decode(const void* k_new, const void* v_new, int64_t k_tok_stri
                         const int32_t* state_idx, const int64_t* slot_mapping, void* k_cache,
                         void* v_cache, int64_t num_slots, int32_t num_heads, int32_t head_dim,
                         int32_t width, int32_t dtype, void* stream);
+
+/*
+ * Speculative verification. Serving engines verify the candidate tokens of a draft model or of
+ * multi-token-prediction heads in one forward pass (aib.vote English news item on SGLang/Miles
+ * Inkling support, paragraph 3; data-sketchers.com SGLang cookbook for Inkling-Small, section 2
+ * on MTP and section 3.7 on DSpark). For the conv state this means: run each sequence's
+ * candidates from its stored state, but install the state of only the prefix that the verifier
+ * accepts, which is known after the call.
+ *
+ * shortconv_kv_verify: as shortconv_kv_prefill with has_initial_state = 1 for every sequence
+ * (the same cache rows, bit for bit), except that the state pools are only READ. The state after
+ * each token goes to the snapshot buffers instead:
+ *  k_snap, v_snap   [num_seqs][max_tokens][W-1][H][D], element type `dtype`: snapshot (s, i) is
+ *                   the conv state after the first i+1 tokens of sequence s (bit copies of raw
+ *                   rows, oldest first), written for i < min(L_s, max_tokens); other entries are
+ *                   not written. May be NULL when width == 1.
+ *  max_tokens       >= 1, the snapshot capacity per sequence (the longest candidate run).
+ * Sequences are processed 16 tokens per pass; candidate runs are meant to be short.
+ */
+int shortconv_kv_verify(const void* k, const void* v, int64_t k_tok_stride, int64_t v_tok_stride,
+                        const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                        const float* k_taps, const float* v_taps, const float* k_gamma,
+                        const float* v_gamma, float eps, const void* k_state, const void* v_state,
+                        int64_t num_state_slots, const int32_t* state_idx, void* k_snap,
+                        void* v_snap, int32_t max_tokens, const int64_t* slot_mapping,
+                        void* k_cache, void* v_cache, int64_t num_slots, int32_t num_heads,
+                        int32_t head_dim, int32_t width, int32_t dtype, void* stream);
+
+/*
+ * shortconv_state_commit: installs the accepted prefix. For sequence s, m = min(accepted[s], L_s,
+ * max_tokens) with L_s = cu_seqlens[s+1] - cu_seqlens[s] (cu_seqlens and total_tokens as given to
+ * shortconv_kv_verify); if m >= 1 and state_idx[s] (or s when state_idx is NULL) is inside the
+ * pool, that pool row becomes snapshot (s, m-1), bit for bit. m == 0 leaves the row unchanged.
+ * accepted: device int32 [num_seqs]. A no-op when width == 1.
+ */
+int shortconv_state_commit(const void* k_snap, const void* v_snap, int32_t max_tokens,
+                           const int32_t* cu_seqlens, int64_t total_tokens,
+                           const int32_t* accepted, int32_t num_seqs, void* k_state,
+                           void* v_state, int64_t num_state_slots, const int32_t* state_idx,
+                           int32_t num_heads, int32_t head_dim, int32_t width, int32_t dtype,
+                           void* stream);
 
 /* Message for the last non-zero return on the calling thread ("" if none). Valid until the next
  * call on the same thread. */

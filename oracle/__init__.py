@@ -219,6 +219,71 @@ def fused_decode(k_new, v_new, k_taps, v_taps, k_gamma, v_gamma, eps, k_state, v
 
 
 # ---------------------------------------------------------------------------------------------
+# Speculative verification: k candidate tokens per sequence run from the stored conv state, and
+# the state after every token is kept so that the state of any accepted prefix can be installed
+# afterwards (speculative decoding with draft models or multi-token-prediction heads: aib.vote
+# English news item on SGLang/Miles Inkling support, paragraph 3; data-sketchers.com SGLang
+# cookbook for Inkling-Small, section 2 (MTP) and section 3.7 (DSpark)).
+# ---------------------------------------------------------------------------------------------
+def verify_snapshots(x, cu_seqlens, state, state_idx, width, max_tokens):
+    """snapshots[s, i] = rows e[i+1 .. i+W-1] of e = [initial window, rows of sequence s], i.e. the
+    conv state after its first i+1 tokens, as bit copies; written for i < min(L_s, max_tokens),
+    zero elsewhere. The initial window is the stored state row (an index outside the pool means
+    zeros). Returns None when W == 1."""
+    R = width - 1
+    if R == 0:
+        return None
+    cu = np.asarray(cu_seqlens, np.int64)
+    N = len(cu) - 1
+    H, D = x.shape[1], x.shape[2]
+    snaps = np.zeros((N, max_tokens, R, H, D), x.dtype)
+    for s in range(N):
+        idx = int(state_idx[s])
+        if state is not None and 0 <= idx < state.shape[0]:
+            z = state[idx]
+        else:
+            z = np.zeros((R, H, D), x.dtype)
+        e = np.concatenate([z, x[cu[s]:cu[s + 1]]], axis=0)
+        for i in range(min(int(cu[s + 1] - cu[s]), max_tokens)):
+            snaps[s, i] = e[i + 1:i + 1 + R]
+    return snaps
+
+
+def commit_state(pool, snapshots, accepted, cu_seqlens, state_idx, max_tokens):
+    """pool[state_idx[s]] = snapshots[s, m-1] with m = min(accepted[s], L_s, max_tokens), for m >= 1
+    and an index inside the pool; other rows keep their bits. Returns the new pool."""
+    if pool is None:
+        return None
+    out = pool.copy()
+    cu = np.asarray(cu_seqlens, np.int64)
+    for s in range(len(cu) - 1):
+        m = min(int(accepted[s]), int(cu[s + 1] - cu[s]), max_tokens)
+        idx = int(state_idx[s])
+        if m >= 1 and 0 <= idx < pool.shape[0]:
+            out[idx] = snapshots[s, m - 1]
+    return out
+
+
+def fused_verify(k, v, cu_seqlens, k_taps, v_taps, k_gamma, v_gamma, eps, k_state, v_state,
+                 state_idx, slot_mapping, num_slots, max_tokens, *, cond=True, nthreads=1):
+    """Verification step for K and V: the outputs are those of a prefill that resumes every
+    sequence from its stored state; the pools are not modified (the result's k_state/v_state are
+    the input pools) and the per-token snapshots are returned as (k_snap, v_snap)."""
+    N = len(cu_seqlens) - 1
+    sidx = np.arange(N) if state_idx is None else np.asarray(state_idx, np.int64)
+    ones = np.ones(N, np.uint8)
+    yk, _, ck = prefill_one(k, cu_seqlens, k_taps, k_gamma, eps, k_state, sidx, ones, cond=cond,
+                            nthreads=nthreads)
+    yv, _, cv = prefill_one(v, cu_seqlens, v_taps, v_gamma, eps, v_state, sidx, ones, cond=cond,
+                            nthreads=nthreads)
+    W = np.asarray(k_taps).shape[0]
+    ks = verify_snapshots(k, cu_seqlens, k_state, sidx, W, max_tokens)
+    vs = verify_snapshots(v, cu_seqlens, v_state, sidx, W, max_tokens)
+    res = StepResult(yk, yv, ck, cv, cache_slots(slot_mapping, num_slots), k_state, v_state)
+    return res, ks, vs
+
+
+# ---------------------------------------------------------------------------------------------
 # The acceptance metric for floating-point outputs (used by the parity tests).
 #
 # A correct kernel that accumulates in fp32 cannot meet a pure element-wise relative bound on

@@ -452,6 +452,47 @@ def pin_cond_scale():
         assert (c2 >= np.abs(y2) * (1 - 1e-14)).all() and (c2 > np.abs(y2) * 1.01).any()
 
 
+def pin_verify_snapshots_and_commit():
+    """Per-token snapshots equal the state a prefill of the first i+1 tokens leaves, and the state
+    token-by-token decode reaches; commit installs the snapshot of the accepted prefix."""
+    for dtype, W in (("bf16", 4), ("f32", 8), ("bf16", 2)):
+        lens = [3, 0, 1, 8, 6]
+        w = _small(dtype=dtype, W=W, lens=lens, hin=[1] * len(lens), H=2, D=64)
+        st = w.steps[0]
+        cu = st.cu_seqlens
+        K = 7  # max_tokens below the longest sequence: its 8th token gets no snapshot
+        r, ks, _ = oracle.fused_verify(st.k, st.v, cu, w.k_taps, w.v_taps, w.k_gamma, w.v_gamma,
+                                       w.eps, w.k_state, w.v_state, st.state_idx, st.slot_mapping,
+                                       w.num_slots, K, cond=False)
+        assert np.array_equal(r.k_state, w.k_state), "verify must not touch the pool"
+        for s in range(len(lens)):
+            a = int(cu[s])
+            pool = w.k_state.copy()
+            for i in range(min(lens[s], K)):
+                # prefill of the first i+1 tokens from the stored state
+                _, ns, _ = oracle.prefill_one(st.k[a:a + i + 1], np.array([0, i + 1]), w.k_taps,
+                                              w.k_gamma, w.eps, w.k_state,
+                                              st.state_idx[s:s + 1], np.array([1]))
+                assert np.array_equal(ks[s, i], ns[0]), f"snapshot {s},{i} != prefill state"
+                # token-by-token decode
+                yd, nd, _ = oracle.decode_one(st.k[a + i:a + i + 1], w.k_taps, w.k_gamma, w.eps,
+                                              pool, st.state_idx[s:s + 1])
+                pool[st.state_idx[s]] = nd[0]
+                assert np.array_equal(ks[s, i], nd[0]), f"snapshot {s},{i} != decode state"
+                assert np.array_equal(yd[0], r.y_k[a + i]), f"verify output {s},{i} != decode"
+        acc = np.array([2, 5, 0, 9, 6])
+        new = oracle.commit_state(w.k_state, ks, acc, cu, st.state_idx, K)
+        for s in range(len(lens)):
+            m = min(acc[s], lens[s], K)
+            if m == 0:
+                assert np.array_equal(new[st.state_idx[s]], w.k_state[st.state_idx[s]])
+            else:
+                _, ns, _ = oracle.prefill_one(st.k[cu[s]:cu[s] + m], np.array([0, m]), w.k_taps,
+                                              w.k_gamma, w.eps, w.k_state,
+                                              st.state_idx[s:s + 1], np.array([1]))
+                assert np.array_equal(new[st.state_idx[s]], ns[0]), f"commit of {s}"
+
+
 ALL_PINS = [
     pin_exact_rational,
     pin_torch_conv1d_rmsnorm,
@@ -467,4 +508,5 @@ ALL_PINS = [
     pin_scale_invariance,
     pin_placement_and_pools,
     pin_cond_scale,
+    pin_verify_snapshots_and_commit,
 ]
