@@ -2,12 +2,14 @@
 
 Causal depthwise convolution over tokens of the projected K and V, per-head RMSNorm, paged
 KV-cache write and rolling conv-state update, in one HIP kernel per call; plus speculative
-verification with per-token conv-state snapshots and the commit of an accepted prefix. The
+verification with per-token conv-state snapshots and the commit of an accepted prefix, and
+variants that write MXFP8 (OCP microscaling) cache rows. The
 compute lives in ``libshortconv.so`` (C ABI, ``include/shortconv.h``); this package only
 marshals torch tensors.
 """
 from ._binding import (LIBRARY_PATH, ShortConvError, abi_version, last_error, load_library,
-                       shortconv_kv_decode, shortconv_kv_prefill, shortconv_kv_verify,
+                       shortconv_kv_decode, shortconv_kv_decode_mxfp8, shortconv_kv_prefill,
+                       shortconv_kv_prefill_mxfp8, shortconv_kv_verify, shortconv_mxfp8_quantize,
                        shortconv_state_commit)
 
 __all__ = [
@@ -17,7 +19,10 @@ __all__ = [
     "last_error",
     "load_library",
     "shortconv_kv_decode",
+    "shortconv_kv_decode_mxfp8",
     "shortconv_kv_prefill",
+    "shortconv_kv_prefill_mxfp8",
+    "shortconv_mxfp8_quantize",
     "shortconv_kv_verify",
     "shortconv_state_commit",
 ]

@@ -52,6 +52,15 @@ def load_library(path: str = LIBRARY_PATH):
     lib.shortconv_state_commit.restype = ctypes.c_int
     lib.shortconv_state_commit.argtypes = [P, P, I32, P, I64, P, I32, P, P, I64, P, I32, I32, I32,
                                            I32, P]
+    lib.shortconv_kv_prefill_mxfp8.restype = ctypes.c_int
+    lib.shortconv_kv_prefill_mxfp8.argtypes = [P, P, I64, I64, P, I32, I64, P, P, P, P, F, P, P,
+                                               I64, P, P, P, P, P, P, P, I64, I32, I32, I32, I32,
+                                               P]
+    lib.shortconv_kv_decode_mxfp8.restype = ctypes.c_int
+    lib.shortconv_kv_decode_mxfp8.argtypes = [P, P, I64, I64, I32, P, P, P, P, F, P, P, I64, P, P,
+                                              P, P, P, P, I64, I32, I32, I32, I32, P]
+    lib.shortconv_mxfp8_quantize.restype = ctypes.c_int
+    lib.shortconv_mxfp8_quantize.argtypes = [P, I64, I64, I32, I32, I32, P, P, P]
     lib.shortconv_last_error.restype = ctypes.c_char_p
     lib.shortconv_last_error.argtypes = []
     lib.shortconv_abi_version.restype = ctypes.c_int
@@ -166,4 +175,55 @@ def shortconv_state_commit(k_snap, v_snap, cu_seqlens, total_tokens, accepted, k
             _ptr(accepted), cu_seqlens.shape[0] - 1, _ptr(k_state), _ptr(v_state), S,
             _ptr(state_idx), num_heads, head_dim, width, SC_DTYPE[dtype],
             _stream_handle(dev, stream))
+    _check(rc)
+
+
+def shortconv_kv_prefill_mxfp8(k, v, cu_seqlens, k_taps, v_taps, k_gamma, v_gamma, eps, k_state,
+                               v_state, state_idx, has_initial_state, slot_mapping, k_codes,
+                               v_codes, k_scales, v_scales, *,
+                               stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Prefill writing MXFP8 cache rows: codes uint8 [num_slots,H,D], scales uint8
+    [num_slots,H,D/32] (see include/shortconv.h)."""
+    lib = load_library()
+    W, H, D = k_taps.shape
+    if has_initial_state is not None and has_initial_state.dtype == torch.bool:
+        has_initial_state = has_initial_state.view(torch.uint8)
+    S = k_state.shape[0] if k_state is not None else 0
+    with torch.cuda.device(k.device):
+        rc = lib.shortconv_kv_prefill_mxfp8(
+            _ptr(k), _ptr(v), _rows(k, "k"), _rows(v, "v"), _ptr(cu_seqlens),
+            cu_seqlens.shape[0] - 1, k.shape[0], _ptr(k_taps), _ptr(v_taps), _ptr(k_gamma),
+            _ptr(v_gamma), float(eps), _ptr(k_state), _ptr(v_state), S, _ptr(state_idx),
+            _ptr(has_initial_state), _ptr(slot_mapping), _ptr(k_codes), _ptr(v_codes),
+            _ptr(k_scales), _ptr(v_scales), k_codes.shape[0], H, D, W, SC_DTYPE[k.dtype],
+            _stream_handle(k.device, stream))
+    _check(rc)
+
+
+def shortconv_kv_decode_mxfp8(k_new, v_new, k_taps, v_taps, k_gamma, v_gamma, eps, k_state,
+                              v_state, state_idx, slot_mapping, k_codes, v_codes, k_scales,
+                              v_scales, *, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Decode writing MXFP8 cache rows (see include/shortconv.h)."""
+    lib = load_library()
+    W, H, D = k_taps.shape
+    S = k_state.shape[0] if k_state is not None else 0
+    with torch.cuda.device(k_new.device):
+        rc = lib.shortconv_kv_decode_mxfp8(
+            _ptr(k_new), _ptr(v_new), _rows(k_new, "k_new"), _rows(v_new, "v_new"),
+            k_new.shape[0], _ptr(k_taps), _ptr(v_taps), _ptr(k_gamma), _ptr(v_gamma), float(eps),
+            _ptr(k_state), _ptr(v_state), S, _ptr(state_idx), _ptr(slot_mapping), _ptr(k_codes),
+            _ptr(v_codes), _ptr(k_scales), _ptr(v_scales), k_codes.shape[0], H, D, W,
+            SC_DTYPE[k_new.dtype], _stream_handle(k_new.device, stream))
+    _check(rc)
+
+
+def shortconv_mxfp8_quantize(x, codes, scales, *,
+                             stream: Optional[torch.cuda.Stream] = None) -> None:
+    """MXFP8-quantize rows x [rows,H,D] into codes [rows,H,D] and scales [rows,H,D/32] (uint8)."""
+    lib = load_library()
+    rows, H, D = x.shape
+    with torch.cuda.device(x.device):
+        rc = lib.shortconv_mxfp8_quantize(_ptr(x), _rows(x, "x"), rows, H, D, SC_DTYPE[x.dtype],
+                                          _ptr(codes), _ptr(scales),
+                                          _stream_handle(x.device, stream))
     _check(rc)

@@ -92,16 +92,16 @@ sc::StepArgs make_args(const void* k, const void* v, int64_t ks, int64_t vs, con
 
 }  // namespace
 
-SC_API int shortconv_kv_prefill(const void* k, const void* v, int64_t k_tok_stride,
-                                int64_t v_tok_stride, const int32_t* cu_seqlens, int32_t num_seqs,
-                                int64_t total_tokens, const float* k_taps, const float* v_taps,
-                                const float* k_gamma, const float* v_gamma, float eps,
-                                void* k_state, void* v_state, int64_t num_state_slots,
-                                const int32_t* state_idx, const uint8_t* has_initial_state,
-                                const int64_t* slot_mapping, void* k_cache, void* v_cache,
-                                int64_t num_slots, int32_t num_heads, int32_t head_dim,
-                                int32_t width, int32_t dtype, void* stream) {
-    const char* fn = "shortconv_kv_prefill";
+namespace {
+
+int prefill_impl(const char* fn, const void* k, const void* v, int64_t k_tok_stride,
+                 int64_t v_tok_stride, const int32_t* cu_seqlens, int32_t num_seqs,
+                 int64_t total_tokens, const float* k_taps, const float* v_taps,
+                 const float* k_gamma, const float* v_gamma, float eps, void* k_state,
+                 void* v_state, int64_t num_state_slots, const int32_t* state_idx,
+                 const uint8_t* has_initial_state, const int64_t* slot_mapping, void* k_cache,
+                 void* v_cache, void* k_scales, void* v_scales, bool mx, int64_t num_slots,
+                 int32_t num_heads, int32_t head_dim, int32_t width, int32_t dtype, void* stream) {
     g_err[0] = 0;
     int rc = check_common(fn, k, v, k_tok_stride, v_tok_stride, k_taps, v_taps, k_gamma, v_gamma,
                           eps, k_state, v_state, num_state_slots, slot_mapping, k_cache, v_cache,
@@ -110,6 +110,8 @@ SC_API int shortconv_kv_prefill(const void* k, const void* v, int64_t k_tok_stri
     if (num_seqs < 0) return fail(SC_ERR_INVALID, "%s: num_seqs < 0", fn);
     if (total_tokens < 0 || total_tokens > INT32_MAX)
         return fail(SC_ERR_INVALID, "%s: total_tokens must be in [0, 2^31)", fn);
+    if (mx && num_slots > 0 && (!k_scales || !v_scales))
+        return fail(SC_ERR_INVALID, "%s: null MXFP8 scale buffer", fn);
     if (num_seqs == 0) return SC_OK;  // no sequence owns any token: nothing to do
     if (!cu_seqlens) return fail(SC_ERR_INVALID, "%s: null cu_seqlens", fn);
     if (width == 1 && total_tokens == 0) return SC_OK;
@@ -117,6 +119,8 @@ SC_API int shortconv_kv_prefill(const void* k, const void* v, int64_t k_tok_stri
     sc::StepArgs a = make_args(k, v, k_tok_stride, v_tok_stride, k_taps, v_taps, k_gamma, v_gamma,
                                eps, k_state, v_state, num_state_slots, state_idx, slot_mapping,
                                k_cache, v_cache, num_slots, num_heads, head_dim, width, dtype);
+    a.scales[0] = k_scales;
+    a.scales[1] = v_scales;
     a.cu = cu_seqlens;
     a.has_init = has_initial_state;
     a.tokens = total_tokens;
@@ -126,9 +130,74 @@ SC_API int shortconv_kv_prefill(const void* k, const void* v, int64_t k_tok_stri
     if (tiles * ((2 * (int64_t)a.lanes_per_tensor + 63) / 64) > INT32_MAX)
         return fail(SC_ERR_UNSUPPORTED, "%s: problem too large for one launch", fn);
     a.tiles = (int32_t)tiles;
-    hipError_t e = sc::launch_prefill(a, dtype, head_dim, width, (hipStream_t)stream);
+    hipError_t e = sc::launch_prefill(a, dtype, head_dim, width, mx, (hipStream_t)stream);
     if (e != hipSuccess) return fail(SC_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return SC_OK;
+}
+
+int decode_impl(const char* fn, const void* k_new, const void* v_new, int64_t k_tok_stride,
+                int64_t v_tok_stride, int32_t batch, const float* k_taps, const float* v_taps,
+                const float* k_gamma, const float* v_gamma, float eps, void* k_state,
+                void* v_state, int64_t num_state_slots, const int32_t* state_idx,
+                const int64_t* slot_mapping, void* k_cache, void* v_cache, void* k_scales,
+                void* v_scales, bool mx, int64_t num_slots, int32_t num_heads, int32_t head_dim,
+                int32_t width, int32_t dtype, void* stream) {
+    g_err[0] = 0;
+    int rc = check_common(fn, k_new, v_new, k_tok_stride, v_tok_stride, k_taps, v_taps, k_gamma,
+                          v_gamma, eps, k_state, v_state, num_state_slots, slot_mapping, k_cache,
+                          v_cache, num_slots, num_heads, head_dim, width, dtype, batch);
+    if (rc != SC_OK) return rc;
+    if (batch < 0) return fail(SC_ERR_INVALID, "%s: batch < 0", fn);
+    if (mx && num_slots > 0 && (!k_scales || !v_scales))
+        return fail(SC_ERR_INVALID, "%s: null MXFP8 scale buffer", fn);
+    if (batch == 0) return SC_OK;
+    sc::StepArgs a = make_args(k_new, v_new, k_tok_stride, v_tok_stride, k_taps, v_taps, k_gamma,
+                               v_gamma, eps, k_state, v_state, num_state_slots, state_idx,
+                               slot_mapping, k_cache, v_cache, num_slots, num_heads, head_dim,
+                               width, dtype);
+    a.scales[0] = k_scales;
+    a.scales[1] = v_scales;
+    a.tokens = batch;
+    if (a.lane_blocks > 65535) return fail(SC_ERR_UNSUPPORTED, "%s: num_heads too large", fn);
+    hipError_t e = sc::launch_decode(a, dtype, head_dim, width, mx, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(SC_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return SC_OK;
+}
+
+}  // namespace
+
+SC_API int shortconv_kv_prefill(const void* k, const void* v, int64_t k_tok_stride,
+                                int64_t v_tok_stride, const int32_t* cu_seqlens, int32_t num_seqs,
+                                int64_t total_tokens, const float* k_taps, const float* v_taps,
+                                const float* k_gamma, const float* v_gamma, float eps,
+                                void* k_state, void* v_state, int64_t num_state_slots,
+                                const int32_t* state_idx, const uint8_t* has_initial_state,
+                                const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                int64_t num_slots, int32_t num_heads, int32_t head_dim,
+                                int32_t width, int32_t dtype, void* stream) {
+    return prefill_impl("shortconv_kv_prefill", k, v, k_tok_stride, v_tok_stride, cu_seqlens,
+                        num_seqs, total_tokens, k_taps, v_taps, k_gamma, v_gamma, eps, k_state,
+                        v_state, num_state_slots, state_idx, has_initial_state, slot_mapping,
+                        k_cache, v_cache, nullptr, nullptr, false, num_slots, num_heads, head_dim,
+                        width, dtype, stream);
+}
+
+SC_API int shortconv_kv_prefill_mxfp8(const void* k, const void* v, int64_t k_tok_stride,
+                                      int64_t v_tok_stride, const int32_t* cu_seqlens,
+                                      int32_t num_seqs, int64_t total_tokens, const float* k_taps,
+                                      const float* v_taps, const float* k_gamma,
+                                      const float* v_gamma, float eps, void* k_state,
+                                      void* v_state, int64_t num_state_slots,
+                                      const int32_t* state_idx, const uint8_t* has_initial_state,
+                                      const int64_t* slot_mapping, void* k_codes, void* v_codes,
+                                      void* k_scales, void* v_scales, int64_t num_slots,
+                                      int32_t num_heads, int32_t head_dim, int32_t width,
+                                      int32_t dtype, void* stream) {
+    return prefill_impl("shortconv_kv_prefill_mxfp8", k, v, k_tok_stride, v_tok_stride,
+                        cu_seqlens, num_seqs, total_tokens, k_taps, v_taps, k_gamma, v_gamma, eps,
+                        k_state, v_state, num_state_slots, state_idx, has_initial_state,
+                        slot_mapping, k_codes, v_codes, k_scales, v_scales, true, num_slots,
+                        num_heads, head_dim, width, dtype, stream);
 }
 
 SC_API int shortconv_kv_decode(const void* k_new, const void* v_new, int64_t k_tok_stride,
@@ -139,21 +208,58 @@ SC_API int shortconv_kv_decode(const void* k_new, const void* v_new, int64_t k_t
                                void* k_cache, void* v_cache, int64_t num_slots,
                                int32_t num_heads, int32_t head_dim, int32_t width, int32_t dtype,
                                void* stream) {
-    const char* fn = "shortconv_kv_decode";
+    return decode_impl("shortconv_kv_decode", k_new, v_new, k_tok_stride, v_tok_stride, batch,
+                       k_taps, v_taps, k_gamma, v_gamma, eps, k_state, v_state, num_state_slots,
+                       state_idx, slot_mapping, k_cache, v_cache, nullptr, nullptr, false,
+                       num_slots, num_heads, head_dim, width, dtype, stream);
+}
+
+SC_API int shortconv_kv_decode_mxfp8(const void* k_new, const void* v_new, int64_t k_tok_stride,
+                                     int64_t v_tok_stride, int32_t batch, const float* k_taps,
+                                     const float* v_taps, const float* k_gamma,
+                                     const float* v_gamma, float eps, void* k_state,
+                                     void* v_state, int64_t num_state_slots,
+                                     const int32_t* state_idx, const int64_t* slot_mapping,
+                                     void* k_codes, void* v_codes, void* k_scales, void* v_scales,
+                                     int64_t num_slots, int32_t num_heads, int32_t head_dim,
+                                     int32_t width, int32_t dtype, void* stream) {
+    return decode_impl("shortconv_kv_decode_mxfp8", k_new, v_new, k_tok_stride, v_tok_stride,
+                       batch, k_taps, v_taps, k_gamma, v_gamma, eps, k_state, v_state,
+                       num_state_slots, state_idx, slot_mapping, k_codes, v_codes, k_scales,
+                       v_scales, true, num_slots, num_heads, head_dim, width, dtype, stream);
+}
+
+SC_API int shortconv_mxfp8_quantize(const void* x, int64_t tok_stride, int64_t rows,
+                                    int32_t num_heads, int32_t head_dim, int32_t dtype,
+                                    void* codes, void* scales, void* stream) {
+    const char* fn = "shortconv_mxfp8_quantize";
     g_err[0] = 0;
-    int rc = check_common(fn, k_new, v_new, k_tok_stride, v_tok_stride, k_taps, v_taps, k_gamma,
-                          v_gamma, eps, k_state, v_state, num_state_slots, slot_mapping, k_cache,
-                          v_cache, num_slots, num_heads, head_dim, width, dtype, batch);
-    if (rc != SC_OK) return rc;
-    if (batch < 0) return fail(SC_ERR_INVALID, "%s: batch < 0", fn);
-    if (batch == 0) return SC_OK;
-    sc::StepArgs a = make_args(k_new, v_new, k_tok_stride, v_tok_stride, k_taps, v_taps, k_gamma,
-                               v_gamma, eps, k_state, v_state, num_state_slots, state_idx,
-                               slot_mapping, k_cache, v_cache, num_slots, num_heads, head_dim,
-                               width, dtype);
-    a.tokens = batch;
-    if (a.lane_blocks > 65535) return fail(SC_ERR_UNSUPPORTED, "%s: num_heads too large", fn);
-    hipError_t e = sc::launch_decode(a, dtype, head_dim, width, (hipStream_t)stream);
+    if (dtype != SC_DTYPE_F32 && dtype != SC_DTYPE_BF16)
+        return fail(SC_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+        return fail(SC_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128, 256}", fn, head_dim);
+    if (num_heads < 1 || (int64_t)num_heads * head_dim > (int64_t)1 << 20)
+        return fail(SC_ERR_INVALID, "%s: bad num_heads %d", fn, num_heads);
+    if (rows < 0 || rows > INT32_MAX) return fail(SC_ERR_INVALID, "%s: rows must be in [0, 2^31)", fn);
+    if (rows == 0) return SC_OK;
+    if (!x || !codes || !scales) return fail(SC_ERR_INVALID, "%s: null pointer", fn);
+    const int eb = element_bytes(dtype);
+    if (tok_stride < (int64_t)num_heads * head_dim || (tok_stride * eb) % 16)
+        return fail(SC_ERR_INVALID, "%s: bad row stride", fn);
+    if (!aligned16(x) || !aligned16(codes))
+        return fail(SC_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
+    sc::StepArgs a = {};
+    a.x[0] = x;
+    a.x_stride[0] = tok_stride;
+    a.cache[0] = codes;
+    a.scales[0] = scales;
+    a.tokens = rows;
+    a.num_slots = rows;
+    a.heads = num_heads;
+    a.lanes_per_tensor = num_heads * (head_dim / (16 / eb));
+    if ((a.lanes_per_tensor + 255) / 256 > 65535)
+        return fail(SC_ERR_UNSUPPORTED, "%s: num_heads too large", fn);
+    hipError_t e = sc::launch_mx_quantize(a, dtype, head_dim, (hipStream_t)stream);
     if (e != hipSuccess) return fail(SC_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return SC_OK;
 }

@@ -188,10 +188,11 @@ __device__ inline void load_params(const float* taps, const float* gamma, int he
     }
 }
 
-// The row math of one output row slice: window win[0..W-1] (win[W-1] = current token).
+// The row math of one output row slice: window win[0..W-1] (win[W-1] = current token); o gets the
+// normalized values in fp32, before the one rounding to the cache format.
 template <class E, int W, int LPH>
-__device__ inline uint4 fused_row(const float (&win)[W][E::VEC], const LaneParams<E, W>& p,
-                                  float eps, float inv_d) {
+__device__ inline void fused_row(const float (&win)[W][E::VEC], const LaneParams<E, W>& p,
+                                 float eps, float inv_d, float (&o)[E::VEC]) {
     constexpr int VEC = E::VEC;
     float c[VEC];
 #pragma unroll
@@ -207,11 +208,109 @@ __device__ inline uint4 fused_row(const float (&win)[W][E::VEC], const LaneParam
     // v_rsq_f32: within ~1 ulp of 1/sqrt, one instruction instead of a correctly rounded square
     // root and divide; it scales exactly under power-of-4 scaling of its input.
     const float inv = __builtin_amdgcn_rsqf(__builtin_fmaf(ss, inv_d, eps));
-    float o[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) o[v] = (c[v] * inv) * p.gam[v];
-    return E::narrow(o);
 }
+
+// ------------------------------------------------------------------------------------------------
+// Cache formats. A Sink takes one finished row slice (VEC fp32 values of one head) and writes it
+// to cache row `slot`, unless the slot is outside [0, num_slots) or the lane is idle.
+// ------------------------------------------------------------------------------------------------
+// Plain rows in the I/O element type (one round-to-nearest-even conversion).
+template <class E>
+struct PlainSink {
+    char* cache;
+    int64_t row_bytes;
+    uint32_t lane_off;
+    int64_t num_slots;
+    __device__ PlainSink(const StepArgs& a, int tensor, int h, int d0, int D)
+        : cache(static_cast<char*>(a.cache[tensor])),
+          row_bytes((int64_t)a.heads * D * E::BYTES),
+          lane_off((uint32_t)(((int64_t)h * D + d0) * E::BYTES)),
+          num_slots(a.num_slots) {}
+    __device__ void put(int64_t slot, bool active, const float (&o)[E::VEC]) const {
+        const uint4 out = E::narrow(o);
+        if (active && slot >= 0 && slot < num_slots) strow(cache + slot * row_bytes, lane_off, out);
+    }
+};
+
+// OCP FP8 E4M3 code of v (finite): nearest value, ties to even, saturating at +-448. Exact:
+// the rounding works on the binary32 pattern (normal range) or on v * 2^9, an exact scaling
+// (subnormal range, steps of 2^-9).
+__device__ inline uint32_t e4m3_code(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t ua = u & 0x7fffffffu;
+    // normal: keep 3 fraction bits, round the 20 below to nearest even; the exponent rebias
+    // (127 - 7) moves to the code's exponent field; a carry out of the fraction is correct.
+    uint32_t n = (ua + 0x7ffffu + ((ua >> 20) & 1u)) >> 20;
+    n = n - (120u << 3);
+    n = n > 0x7eu ? 0x7eu : n;  // beyond 448 (including rounding up to 480): saturate
+    const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(ua) * 512.0f);
+    const uint32_t code = ua >= 0x3c800000u ? n : sub;  // 0x3c800000 = 2^-6, the smallest normal
+    return code | sign;
+}
+
+// MXFP8 rows: 32-element blocks along head_dim share one E8M0 scale 2^e with
+// e = floor(log2(max |v|)) - 8 (clamped to [-127, 127]; -127 for an all-zero block), and each
+// element is stored as the E4M3 code of v * 2^-e. Codes [num_slots][H][D] bytes, scales
+// [num_slots][H][D/32] bytes (e + 127). The 32/VEC lanes of a block exchange their maxima by DPP.
+template <class E>
+struct MxSink {
+    static constexpr int VEC = E::VEC;
+    static constexpr int LPB = 32 / VEC;  // lanes per block: 4 (bf16) or 8 (fp32)
+    char* codes;
+    char* scales;
+    int64_t row_elems;
+    uint32_t code_off;
+    uint32_t scale_off;
+    bool scale_lane;
+    int64_t num_slots;
+    __device__ MxSink(const StepArgs& a, int tensor, int h, int d0, int D)
+        : codes(static_cast<char*>(a.cache[tensor])),
+          scales(static_cast<char*>(a.scales[tensor])),
+          row_elems((int64_t)a.heads * D),
+          code_off((uint32_t)((int64_t)h * D + d0)),
+          scale_off((uint32_t)(((int64_t)h * D + d0) / 32)),
+          scale_lane(d0 % 32 == 0),
+          num_slots(a.num_slots) {}
+    __device__ void put(int64_t slot, bool active, const float (&o)[VEC]) const {
+        float amax = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) amax = __builtin_fmaxf(amax, __builtin_fabsf(o[v]));
+        amax = __builtin_fmaxf(amax, dpp<kQuadXor1>(amax));
+        amax = __builtin_fmaxf(amax, dpp<kQuadXor2>(amax));
+        if (LPB == 8) amax = __builtin_fmaxf(amax, dpp<kRowHalfMirror>(amax));
+        int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 1 - 8 : -127;
+        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+        uint32_t packed[VEC / 4];
+#pragma unroll
+        for (int q = 0; q < VEC / 4; ++q) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                w |= e4m3_code(__builtin_ldexpf(o[4 * q + b], -e)) << (8 * b);
+            packed[q] = w;
+        }
+        if (!(active && slot >= 0 && slot < num_slots)) return;
+        char* row = codes + slot * row_elems + code_off;
+        if (VEC == 8) {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 w = {packed[0], packed[VEC / 4 - 1]};
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(row));
+        } else {
+            __builtin_nontemporal_store(packed[0], reinterpret_cast<uint32_t*>(row));
+        }
+        if (scale_lane)
+            *reinterpret_cast<uint8_t*>(scales + slot * (row_elems / 32) + scale_off) =
+                (uint8_t)(e + 127);
+    }
+};
+
+template <class E, bool MX>
+struct SinkFor { using type = PlainSink<E>; };
+template <class E>
+struct SinkFor<E, true> { using type = MxSink<E>; };
 
 __device__ inline int32_t clamp_tok(int32_t v, int64_t T) {
     return v < 0 ? 0 : (v > T ? (int32_t)T : v);
@@ -247,7 +346,7 @@ __device__ inline int find_tile_seq(const int32_t* cu, int n, int64_t T, int64_t
     return uniform(base);
 }
 
-template <class E, int D, int W, int BT>
+template <class E, int D, int W, int BT, bool MX>
 __global__ void __launch_bounds__(kBlock, SC_PREFILL_MIN_WAVES) prefill_kernel(StepArgs a) {
     constexpr int VEC = E::VEC;
     constexpr int LPH = D / VEC;
@@ -288,7 +387,7 @@ __global__ void __launch_bounds__(kBlock, SC_PREFILL_MIN_WAVES) prefill_kernel(S
 
     const char* x = static_cast<const char*>(a.x[tensor]);
     const int64_t stride_bytes = a.x_stride[tensor] * E::BYTES;
-    char* cache = static_cast<char*>(a.cache[tensor]);
+    const typename SinkFor<E, MX>::type sink(a, tensor, h, d0, D);
     char* state = static_cast<char*>(a.state[tensor]);
     const int64_t row_bytes = (int64_t)a.heads * D * E::BYTES;
     const uint32_t lane_off = (uint32_t)(((int64_t)h * D + d0) * E::BYTES);
@@ -363,9 +462,9 @@ __global__ void __launch_bounds__(kBlock, SC_PREFILL_MIN_WAVES) prefill_kernel(S
     for (int i = 0; i < BT; ++i) {
         if (i < n) {
             E::widen(raw[i], win[R]);
-            const uint4 out = fused_row<E, W, LPH>(win, p, a.eps, inv_d);
-            if (active && slot[i] >= 0 && slot[i] < a.num_slots)
-                strow(cache + slot[i] * row_bytes, lane_off, out);
+            float o[VEC];
+            fused_row<E, W, LPH>(win, p, a.eps, inv_d, o);
+            sink.put(slot[i], active, o);
 #pragma unroll
             for (int k = 0; k < R; ++k)
 #pragma unroll
@@ -395,7 +494,7 @@ __global__ void __launch_bounds__(kBlock, SC_PREFILL_MIN_WAVES) prefill_kernel(S
 // ------------------------------------------------------------------------------------------------
 // Decode: one token per sequence; window = [state rows 0..W-2, new row]; state shifts by one.
 // ------------------------------------------------------------------------------------------------
-template <class E, int D, int W>
+template <class E, int D, int W, bool MX>
 __global__ void __launch_bounds__(kBlock) decode_kernel(StepArgs a) {
     constexpr int VEC = E::VEC;
     constexpr int LPH = D / VEC;
@@ -428,10 +527,10 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(StepArgs a) {
     float win[W][VEC];
 #pragma unroll
     for (int k = 0; k < W; ++k) E::widen(raw[k], win[k]);
-    const uint4 out = fused_row<E, W, LPH>(win, p, a.eps, 1.0f / (float)D);
-
-    if (slot >= 0 && slot < a.num_slots)
-        strow(static_cast<char*>(a.cache[tensor]) + slot * row_bytes, lane_off, out);
+    float o[VEC];
+    fused_row<E, W, LPH>(win, p, a.eps, 1.0f / (float)D, o);
+    const typename SinkFor<E, MX>::type sink(a, tensor, h, d0, D);
+    sink.put(slot, true, o);
     if (slot_ok) {
 #pragma unroll
         for (int k = 0; k < R; ++k) strow(srow + k * row_bytes, lane_off, raw[k + 1]);
@@ -462,7 +561,7 @@ __global__ void __launch_bounds__(kBlock) verify_kernel(StepArgs a, VerifyArgs v
     const uint32_t lane_off = (uint32_t)(((int64_t)h * D + d0) * E::BYTES);
     const char* x = static_cast<const char*>(a.x[tensor]);
     const int64_t stride_bytes = a.x_stride[tensor] * E::BYTES;
-    char* cache = static_cast<char*>(a.cache[tensor]);
+    const PlainSink<E> sink(a, tensor, h, d0, D);
     const char* state = static_cast<const char*>(a.state[tensor]);
     char* snap = static_cast<char*>(va.snap[tensor]);
 
@@ -502,9 +601,9 @@ __global__ void __launch_bounds__(kBlock) verify_kernel(StepArgs a, VerifyArgs v
         for (int i = 0; i < K; ++i) {
             if (c0 + i < L) {
                 E::widen(raw[i], win[R]);
-                const uint4 out = fused_row<E, W, LPH>(win, p, a.eps, inv_d);
-                if (slot[i] >= 0 && slot[i] < a.num_slots)
-                    strow(cache + slot[i] * row_bytes, lane_off, out);
+                float o[VEC];
+                fused_row<E, W, LPH>(win, p, a.eps, inv_d, o);
+                sink.put(slot[i], true, o);
 #pragma unroll
                 for (int k = 0; k < R; ++k)
 #pragma unroll
@@ -562,6 +661,27 @@ __global__ void __launch_bounds__(kBlock) commit_kernel(StepArgs a, VerifyArgs v
 }
 
 // ------------------------------------------------------------------------------------------------
+// Standalone MXFP8 quantization of rows [rows][H][D] (e.g. to convert an existing cache), with
+// exactly the quantizer the fused kernels use.
+// ------------------------------------------------------------------------------------------------
+template <class E, int D>
+__global__ void __launch_bounds__(kBlock) mx_quantize_kernel(StepArgs a) {
+    constexpr int VEC = E::VEC;
+    constexpr int LPH = D / VEC;
+    const int64_t r = blockIdx.x;
+    const int lane = blockIdx.y * kBlock + threadIdx.x;
+    if (lane >= a.lanes_per_tensor) return;
+    const int h = lane / LPH;
+    const int d0 = (lane - h * LPH) * VEC;
+    const uint4 raw = ldrow(static_cast<const char*>(a.x[0]) + r * a.x_stride[0] * E::BYTES,
+                            (uint32_t)(((int64_t)h * D + d0) * E::BYTES));
+    float o[VEC];
+    E::widen(raw, o);
+    const MxSink<E> sink(a, 0, h, d0, D);
+    sink.put(r, true, o);
+}
+
+// ------------------------------------------------------------------------------------------------
 // Dispatch tables: [dtype][head_dim index][width - 1]
 // ------------------------------------------------------------------------------------------------
 using KernelFn = void (*)(StepArgs);
@@ -570,9 +690,13 @@ template <int W>
 constexpr int tile_tokens() { return W <= 4 ? SC_PREFILL_TILE : SC_PREFILL_TILE_WIDE; }
 
 template <class E, int D, int W>
-constexpr KernelFn prefill_fn() { return prefill_kernel<E, D, W, tile_tokens<W>()>; }
+constexpr KernelFn prefill_fn() { return prefill_kernel<E, D, W, tile_tokens<W>(), false>; }
 template <class E, int D, int W>
-constexpr KernelFn decode_fn() { return decode_kernel<E, D, W>; }
+constexpr KernelFn prefill_mx_fn() { return prefill_kernel<E, D, W, tile_tokens<W>(), true>; }
+template <class E, int D, int W>
+constexpr KernelFn decode_fn() { return decode_kernel<E, D, W, false>; }
+template <class E, int D, int W>
+constexpr KernelFn decode_mx_fn() { return decode_kernel<E, D, W, true>; }
 using VerifyFn = void (*)(StepArgs, VerifyArgs);
 template <class E, int D, int W>
 constexpr VerifyFn verify_fn() { return verify_kernel<E, D, W>; }
@@ -590,6 +714,12 @@ constexpr VerifyFn commit_fn() { return commit_kernel<E, D, W>; }
 
 const KernelFn kPrefill[2][3][8] = SC_TABLE(prefill);
 const KernelFn kDecode[2][3][8] = SC_TABLE(decode);
+const KernelFn kPrefillMx[2][3][8] = SC_TABLE(prefill_mx);
+const KernelFn kDecodeMx[2][3][8] = SC_TABLE(decode_mx);
+const KernelFn kQuantizeMx[2][3] = {
+    {mx_quantize_kernel<F32, 64>, mx_quantize_kernel<F32, 128>, mx_quantize_kernel<F32, 256>},
+    {mx_quantize_kernel<BF16, 64>, mx_quantize_kernel<BF16, 128>, mx_quantize_kernel<BF16, 256>},
+};
 const VerifyFn kVerify[2][3][8] = SC_TABLE(verify);
 const VerifyFn kCommit[2][3][8] = SC_TABLE(commit);
 
@@ -601,22 +731,24 @@ int prefill_tile_tokens(int, int, int width) {
     return (kBlock / 64) * (width <= 4 ? tile_tokens<1>() : tile_tokens<8>());
 }
 
-hipError_t launch_prefill(StepArgs a, int dtype, int head_dim, int width, hipStream_t stream) {
+hipError_t launch_prefill(StepArgs a, int dtype, int head_dim, int width, bool mx,
+                          hipStream_t stream) {
     // One workgroup per (tile of 4 * tile_tokens tokens, 64-lane (1 KiB) column slice of the
     // K|V rows); a.lane_blocks carries the number of slices.
     a.lane_blocks = (int32_t)((2 * (int64_t)a.lanes_per_tensor + 63) / 64);
     const int64_t blocks = (int64_t)a.tiles * a.lane_blocks;
-    hipLaunchKernelGGL(kPrefill[dtype][d_index(head_dim)][width - 1], dim3((unsigned)blocks),
-                       dim3(kBlock), 0, stream, a);
+    const KernelFn k = (mx ? kPrefillMx : kPrefill)[dtype][d_index(head_dim)][width - 1];
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kBlock), 0, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_decode(StepArgs a, int dtype, int head_dim, int width, hipStream_t stream) {
+hipError_t launch_decode(StepArgs a, int dtype, int head_dim, int width, bool mx,
+                         hipStream_t stream) {
     const int64_t lanes = 2 * (int64_t)a.lanes_per_tensor;
     const int block = lanes >= kBlock ? kBlock : (int)((lanes + 63) / 64 * 64);
-    hipLaunchKernelGGL(kDecode[dtype][d_index(head_dim)][width - 1],
-                       dim3((unsigned)a.tokens, (unsigned)a.lane_blocks), dim3(block), 0, stream,
-                       a);
+    const KernelFn k = (mx ? kDecodeMx : kDecode)[dtype][d_index(head_dim)][width - 1];
+    hipLaunchKernelGGL(k, dim3((unsigned)a.tokens, (unsigned)a.lane_blocks), dim3(block), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
@@ -637,6 +769,15 @@ hipError_t launch_commit(StepArgs a, VerifyArgs va, int dtype, int head_dim, int
     hipLaunchKernelGGL(kCommit[dtype][d_index(head_dim)][width - 1],
                        dim3((unsigned)a.num_seqs, (unsigned)a.lane_blocks), dim3(block), 0, stream,
                        a, va);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize(StepArgs a, int dtype, int head_dim, hipStream_t stream) {
+    const int64_t lanes = a.lanes_per_tensor;
+    const int block = lanes >= kBlock ? kBlock : (int)((lanes + 63) / 64 * 64);
+    hipLaunchKernelGGL(kQuantizeMx[dtype][d_index(head_dim)],
+                       dim3((unsigned)a.tokens, (unsigned)((lanes + kBlock - 1) / kBlock)),
+                       dim3(block), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -13,7 +13,8 @@ struct StepArgs {
     const float* taps[2];    // fp32 [W][H][D]
     const float* gamma[2];   // fp32 [D]
     void* state[2];          // [num_state_slots][W-1][H][D] or null (W == 1)
-    void* cache[2];          // [num_slots][H][D]
+    void* cache[2];          // [num_slots][H][D] rows, or MXFP8 codes [num_slots][H][D] bytes
+    void* scales[2];         // MXFP8 scales [num_slots][H][D/32] bytes (null for plain rows)
     const int32_t* cu;       // prefill: int32 [num_seqs+1]
     const int32_t* state_idx;  // int32 [num_seqs] or null (identity)
     const uint8_t* has_init;   // prefill: uint8 [num_seqs] or null (all 1)
@@ -37,8 +38,11 @@ struct VerifyArgs {
 };
 
 // Returns hipSuccess or the launch error. `dtype`: 0 = fp32, 1 = bf16. Shapes already validated.
-hipError_t launch_prefill(StepArgs a, int dtype, int head_dim, int width, hipStream_t stream);
-hipError_t launch_decode(StepArgs a, int dtype, int head_dim, int width, hipStream_t stream);
+hipError_t launch_prefill(StepArgs a, int dtype, int head_dim, int width, bool mx,
+                          hipStream_t stream);
+hipError_t launch_decode(StepArgs a, int dtype, int head_dim, int width, bool mx,
+                         hipStream_t stream);
+hipError_t launch_mx_quantize(StepArgs a, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_verify(StepArgs a, VerifyArgs va, int dtype, int head_dim, int width,
                          hipStream_t stream);
 hipError_t launch_commit(StepArgs a, VerifyArgs va, int dtype, int head_dim, int width,

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SHORTCONV_ABI_VERSION 2
+#define SHORTCONV_ABI_VERSION 3
 
 typedef enum {
     SC_DTYPE_F32 = 0,  /* IEEE binary32 */
@@ -119,6 +119,52 @@ int shortconv_kv_decode(const void* k_new, const void* v_new, int64_t k_tok_stri
                         const int32_t* state_idx, const int64_t* slot_mapping, void* k_cache,
                         void* v_cache, int64_t num_slots, int32_t num_heads, int32_t head_dim,
                         int32_t width, int32_t dtype, void* stream);
+
+/*
+ * MXFP8 cache rows. The serving cookbook's long-context recipe stores KV entries as block-scaled
+ * MXFP8 instead of BF16, about doubling the tokens the pools hold (data-sketchers.com SGLang
+ * cookbook for Inkling-Small, section 3.6). The page names the format only; the layout here is
+ * the OCP Microscaling (MX) v1.0 one:
+ *   - each (token, head) row of D elements is split into D/32 blocks of 32 consecutive elements;
+ *   - a block has one E8M0 scale 2^e, e = floor(log2(max |y|)) - 8 clamped to [-127, 127]
+ *     (an all-zero block gets e = -127), stored as the byte e + 127;
+ *   - each element is stored as the OCP FP8 E4M3 code of y * 2^-e (bias 7, no infinity, largest
+ *     finite 448): nearest value, ties to even, saturating at +-448.
+ * Only the cache changes: the conv state stays in the I/O element type, so resuming a sequence is
+ * exact. y is the same fp32 value the plain entry points round to bf16/fp32.
+ *
+ *  k_codes, v_codes    [num_slots][H][D] bytes (16-byte aligned), written at the mapped rows.
+ *  k_scales, v_scales  [num_slots][H][D/32] bytes, written at the mapped rows.
+ * All other arguments are those of shortconv_kv_prefill / shortconv_kv_decode.
+ */
+int shortconv_kv_prefill_mxfp8(const void* k, const void* v, int64_t k_tok_stride,
+                               int64_t v_tok_stride, const int32_t* cu_seqlens, int32_t num_seqs,
+                               int64_t total_tokens, const float* k_taps, const float* v_taps,
+                               const float* k_gamma, const float* v_gamma, float eps,
+                               void* k_state, void* v_state, int64_t num_state_slots,
+                               const int32_t* state_idx, const uint8_t* has_initial_state,
+                               const int64_t* slot_mapping, void* k_codes, void* v_codes,
+                               void* k_scales, void* v_scales, int64_t num_slots,
+                               int32_t num_heads, int32_t head_dim, int32_t width, int32_t dtype,
+                               void* stream);
+
+int shortconv_kv_decode_mxfp8(const void* k_new, const void* v_new, int64_t k_tok_stride,
+                              int64_t v_tok_stride, int32_t batch, const float* k_taps,
+                              const float* v_taps, const float* k_gamma, const float* v_gamma,
+                              float eps, void* k_state, void* v_state, int64_t num_state_slots,
+                              const int32_t* state_idx, const int64_t* slot_mapping,
+                              void* k_codes, void* v_codes, void* k_scales, void* v_scales,
+                              int64_t num_slots, int32_t num_heads, int32_t head_dim,
+                              int32_t width, int32_t dtype, void* stream);
+
+/*
+ * The same MXFP8 quantizer on its own: rows x [rows][H][D] (element type `dtype`, row stride
+ * tok_stride elements) -> codes [rows][H][D] and scales [rows][H][D/32] bytes. For converting
+ * existing cache rows; it applies exactly the rounding the fused entry points apply.
+ */
+int shortconv_mxfp8_quantize(const void* x, int64_t tok_stride, int64_t rows, int32_t num_heads,
+                             int32_t head_dim, int32_t dtype, void* codes, void* scales,
+                             void* stream);
 
 /*
  * Speculative verification. Serving engines verify the candidate tokens of a draft model or of

@@ -284,6 +284,80 @@ def fused_verify(k, v, cu_seqlens, k_taps, v_taps, k_gamma, v_gamma, eps, k_stat
 
 
 # ---------------------------------------------------------------------------------------------
+# MXFP8 cache rows. The cookbook's long-context recipe stores KV entries as block-scaled MXFP8
+# instead of BF16, roughly doubling the tokens the pools hold (data-sketchers.com SGLang cookbook
+# for Inkling-Small, section 3.6). Reading (the page names the format only): the OCP Microscaling
+# (MX) v1.0 layout -- blocks of 32 consecutive elements along head_dim share one E8M0 scale
+# X = 2^(floor(log2(max |v|)) - 8), clamped to [2^-127, 2^127] (an all-zero block gets 2^-127);
+# each element is v / X rounded to OCP FP8 E4M3 (bias 7, no infinity, max normal 448) to nearest,
+# ties to even, saturating at +-448. Scale byte = exponent + 127.
+# ---------------------------------------------------------------------------------------------
+MX_BLOCK = 32
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes):
+    """Value of each OCP E4M3 code (NaN for S.1111.111)."""
+    c = np.asarray(codes, np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    val = np.where((e == 0xF) & (m == 7), np.nan, val)
+    return sign * val
+
+
+def e4m3_encode(v):
+    """Nearest OCP E4M3 code (ties to even), saturating at +-448; v finite (float64 array)."""
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    sign = np.where(np.signbit(v), 0x80, 0).astype(np.int64)
+    mant, ex = np.frexp(a)                    # a = mant * 2^ex, mant in [0.5, 1)
+    e = ex - 1                                # floor(log2 a) for a > 0
+    normal = a >= 2.0 ** -6
+    # normal range: 3 fraction bits at exponent e
+    m = np.rint((a / np.ldexp(1.0, e) - 1.0) * 8.0)   # exact scaling; rint rounds half to even
+    up = m >= 8                               # rounding carried into the next binade
+    e = np.where(up, e + 1, e)
+    m = np.where(up, 0, m)
+    code_n = ((e + 7) << 3) | m.astype(np.int64)
+    # subnormal range: multiples of 2^-9 (a count of 8 is the smallest normal, code 0x08)
+    code_s = np.rint(a * 2.0 ** 9).astype(np.int64)
+    code = np.where(normal, code_n, code_s)
+    code = np.where(a > E4M3_MAX, 0x7E, code)   # beyond the largest normal (incl. rounding up to 480)
+    code = np.where(code > 0x7E, 0x7E, code)
+    return (code | sign).astype(np.uint8)
+
+
+def mx_scale_exponent(block_amax):
+    """floor(log2(amax)) - 8, clamped to [-127, 127]; -127 for an all-zero block."""
+    a = np.asarray(block_amax, np.float64)
+    _, ex = np.frexp(a)
+    e = np.where(a > 0, ex - 1 - 8, -127)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def mxfp8_quantize(y):
+    """y float64 [..., D] (D a multiple of 32) -> (codes uint8 [..., D], scales uint8 [..., D/32])."""
+    y = np.asarray(y, np.float64)
+    D = y.shape[-1]
+    assert D % MX_BLOCK == 0
+    blocks = y.reshape(*y.shape[:-1], D // MX_BLOCK, MX_BLOCK)
+    e = mx_scale_exponent(np.abs(blocks).max(axis=-1))
+    scaled = blocks / np.ldexp(1.0, e)[..., None]
+    codes = e4m3_encode(scaled).reshape(y.shape)
+    return codes, (e + 127).astype(np.uint8)
+
+
+def mxfp8_dequantize(codes, scales):
+    c = np.asarray(codes)
+    D = c.shape[-1]
+    vals = e4m3_decode(c).reshape(*c.shape[:-1], D // MX_BLOCK, MX_BLOCK)
+    x = np.ldexp(1.0, np.asarray(scales, np.int64) - 127)[..., None]
+    return (vals * x).reshape(c.shape)
+
+
+# ---------------------------------------------------------------------------------------------
 # The acceptance metric for floating-point outputs (used by the parity tests).
 #
 # A correct kernel that accumulates in fp32 cannot meet a pure element-wise relative bound on

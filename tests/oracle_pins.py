@@ -493,6 +493,52 @@ def pin_verify_snapshots_and_commit():
                 assert np.array_equal(new[st.state_idx[s]], ns[0]), f"commit of {s}"
 
 
+def pin_mxfp8_codes():
+    """E4M3: every finite code decodes and re-encodes to itself; every midpoint between adjacent
+    values rounds to the even code and a hair either side rounds to the nearer one; values beyond
+    448 saturate; the smallest subnormal and normal sit where the format puts them."""
+    codes = np.arange(0x00, 0x7F, dtype=np.uint8)            # +0 .. 448, NaN (0x7F) excluded
+    vals = oracle.e4m3_decode(codes)
+    assert vals[0x01] == 2.0 ** -9 and vals[0x08] == 2.0 ** -6 and vals[0x7E] == 448.0
+    assert np.isnan(oracle.e4m3_decode(np.array([0x7F, 0xFF]))).all()
+    assert np.array_equal(oracle.e4m3_encode(vals), codes)
+    assert np.array_equal(oracle.e4m3_encode(-vals[1:]), codes[1:] | 0x80)
+    mids = (vals[:-1] + vals[1:]) / 2.0
+    even = np.where(codes[:-1] % 2 == 0, codes[:-1], codes[1:])
+    assert np.array_equal(oracle.e4m3_encode(mids), even), "ties must go to the even code"
+    gap = vals[1:] - vals[:-1]
+    assert np.array_equal(oracle.e4m3_encode(mids - gap * 1e-6), codes[:-1])
+    assert np.array_equal(oracle.e4m3_encode(mids + gap * 1e-6), codes[1:])
+    big = np.array([448.0, 448.5, 463.99, 464.0, 480.0, 511.9, 1e6])
+    assert (oracle.e4m3_encode(big) == 0x7E).all() and (oracle.e4m3_encode(-big) == 0xFE).all()
+
+
+def pin_mxfp8_blocks():
+    """Shared scale = 2^(floor(log2 amax) - 8) per 32-element block; an all-zero block gets the
+    smallest scale; dequantized values sit within half a code step (relative 2^-4) of the input
+    unless the element saturates at 448 * X."""
+    y = np.zeros((3, 64))
+    y[0, :32] = np.linspace(-1.0, 1.0, 32)               # amax = 1 -> exponent -8
+    y[0, 32:] = 3.0 * 2.0 ** -20                          # amax in [2^-19, 2^-18) -> -27
+    y[1, :32] = 0.0
+    y[1, 32:] = 1.99                                      # scaled 509.4 -> saturates to 448
+    y[2] = np.random.default_rng(5).standard_normal(64) * 40.0
+    codes, scales = oracle.mxfp8_quantize(y)
+    assert scales[0, 0] == 127 - 8 and scales[0, 1] == 127 - 27
+    assert scales[1, 0] == 0 and (codes[1, :32] == 0).all()
+    assert (codes[1, 32:] == 0x7E).all() and scales[1, 1] == 127 - 8
+    assert codes[0, 31] == 0x78 and codes[0, 0] == 0xF8  # +-1.0 -> +-256 = 2^8 -> exponent field 15
+    deq = oracle.mxfp8_dequantize(codes, scales)
+    blocks = y.reshape(3, 2, 32)
+    x = np.ldexp(1.0, scales.astype(np.int64) - 127)[..., None]
+    sat = (np.abs(blocks) > 448.0 * x).reshape(3, 64)
+    sub = (np.abs(blocks) < 2.0 ** -6 * x).reshape(3, 64)
+    err = np.abs(deq - y)
+    ok = ~sat & ~sub
+    assert (err[ok] <= 2.0 ** -4 * np.abs(y[ok]) * (1 + 1e-12)).all()
+    assert np.allclose(deq[sat], np.sign(y[sat]) * 448.0 * np.repeat(x.reshape(3, 2), 32, 1)[sat])
+
+
 ALL_PINS = [
     pin_exact_rational,
     pin_torch_conv1d_rmsnorm,
@@ -509,4 +555,6 @@ ALL_PINS = [
     pin_placement_and_pools,
     pin_cond_scale,
     pin_verify_snapshots_and_commit,
+    pin_mxfp8_codes,
+    pin_mxfp8_blocks,
 ]

@@ -31,8 +31,10 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["shortconv_abi_version", "shortconv_kv_decode",
-                                    "shortconv_kv_prefill", "shortconv_kv_verify",
-                                    "shortconv_last_error", "shortconv_state_commit"]
+                                    "shortconv_kv_decode_mxfp8", "shortconv_kv_prefill",
+                                    "shortconv_kv_prefill_mxfp8", "shortconv_kv_verify",
+                                    "shortconv_last_error", "shortconv_mxfp8_quantize",
+                                    "shortconv_state_commit"]
 
 
 def test_library_exports_every_declared_symbol(lib):

@@ -1,0 +1,189 @@
+"""GPU parity of the MXFP8 cache-row variants and of the standalone MXFP8 quantizer.
+
+Where floating point decides a code, both sides decide from the same value: the standalone
+quantizer is fed exactly representable inputs, and the fused path is checked against the oracle's
+quantizer applied to the fused kernel's own fp32 output (fp32 I/O, where that output is what the
+plain entry point stores). For bf16 I/O, where the fp32 output is not observable, codes must lie
+within one E4M3 step of the oracle's and scales must agree except at power-of-two boundaries.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_harness import DEV, DeviceWorkload, rows_to_dev, to_dev, to_host
+from causal_short_convolution_amd import (shortconv_kv_decode_mxfp8, shortconv_kv_prefill_mxfp8,
+                                          shortconv_mxfp8_quantize)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _stored(vals, dtype):
+    f = np.asarray(vals, np.float32)
+    if dtype == "f32":
+        return f
+    b = workloads.to_bf16_bits(f)
+    assert np.array_equal(workloads.bf16_bits_to_f32(b), f)
+    return b
+
+
+def _quantize_on_gpu(x):
+    rows, H, D = x.shape
+    xd = rows_to_dev(x)
+    codes = torch.full((rows, H, D), 0xA5, dtype=torch.uint8, device=DEV)
+    scales = torch.full((rows, H, D // 32), 0xA5, dtype=torch.uint8, device=DEV)
+    shortconv_mxfp8_quantize(xd, codes, scales)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy()
+
+
+def _adversarial_rows(D):
+    """Blocks that sit on every decision the quantizer makes: E4M3 ties (all code midpoints),
+    the saturation boundary 448/464/480, subnormal ties, zeros of both signs, an all-zero
+    block, and block maxima just below the next power of two (elements that saturate)."""
+    vals = oracle.e4m3_decode(np.arange(0x00, 0x7F))
+    mids = (vals[:-1] + vals[1:]) / 2.0
+    pool = np.concatenate([mids, vals, [460.0, 464.0, 470.0, 480.0, 500.0, 0.0, -0.0]])
+    rows = []
+    g = np.random.default_rng(3)
+    for e in (-8, -3, 0, 5, 20):
+        for _ in range(4):
+            r = g.choice(pool, size=D) * g.choice([-1.0, 1.0], size=D)
+            r[::32] = 256.0  # every block's maximum sets the scale to 2^0 before rescaling
+            rows.append(r * 2.0 ** e)
+    r = np.zeros(D)
+    r[32:] = 1.9921875 * 2.0 ** g.integers(-30, 30, size=D - 32)   # maxima just under 2^(k+1)
+    rows.append(r)
+    return np.array(rows)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_quantizer_is_exact(dtype, D):
+    H = 2
+    adv = _adversarial_rows(D)
+    g = np.random.default_rng(D)
+    rnd = g.standard_normal((40, D)) * np.exp2(g.integers(-12, 12, size=(40, 1)))
+    rnd[5, :40] = 0.0
+    vals = np.concatenate([adv, rnd]).astype(np.float32)
+    vals = vals[: len(vals) // H * H]          # whole (row, head) groups
+    if dtype == "bf16":
+        vals = workloads.bf16_bits_to_f32(workloads.to_bf16_bits(vals))
+    x = _stored(vals.reshape(-1, H, D), dtype)
+    codes, scales = _quantize_on_gpu(x)
+    ec, es = oracle.mxfp8_quantize(oracle.widen(x))
+    assert np.array_equal(scales, es), "scale bytes differ"
+    assert np.array_equal(codes, ec), f"codes differ at {np.argwhere(codes != ec)[:5].tolist()}"
+
+
+def test_quantizer_extreme_exponents():
+    """Block maxima far outside E4M3's own range: the scale exponent clamps at -127/+127."""
+    D = 64
+    rows = np.zeros((4, D), np.float32)
+    rows[0, :32] = np.float32(2.0 ** -130) * np.arange(1, 33)   # subnormal inputs, clamp at -127
+    rows[1, :32] = np.float32(2.0 ** 126) * np.linspace(-1, 1, 32)  # scale 2^118
+    rows[2, 32:] = np.float32(2.0 ** -100)
+    rows[3] = np.float32(3.0e38)
+    x = rows.reshape(4, 1, D)
+    codes, scales = _quantize_on_gpu(x)
+    ec, es = oracle.mxfp8_quantize(oracle.widen(x))
+    assert np.array_equal(scales, es) and np.array_equal(codes, ec)
+
+
+def _fused_pair(w):
+    """Run the plain and the MXFP8 prefill+decode on identical copies; return both device runs."""
+    plain = DeviceWorkload(w)
+    plain.run()
+    mx = DeviceWorkload(w, caches=False)
+    H, D = w.H, w.D
+    mx.k_codes = torch.full((w.num_slots, H, D), 0xA5, dtype=torch.uint8, device=DEV)
+    mx.v_codes = torch.full_like(mx.k_codes, 0xA5)
+    mx.k_scales = torch.full((w.num_slots, H, D // 32), 0xA5, dtype=torch.uint8, device=DEV)
+    mx.v_scales = torch.full_like(mx.k_scales, 0xA5)
+    for d in mx.steps:
+        if d["kind"] == "prefill":
+            shortconv_kv_prefill_mxfp8(d["k"], d["v"], d["cu"], mx.k_taps, mx.v_taps, mx.k_gamma,
+                                       mx.v_gamma, w.eps, mx.k_state, mx.v_state, d["sidx"],
+                                       d["hinit"], d["slot"], mx.k_codes, mx.v_codes,
+                                       mx.k_scales, mx.v_scales)
+        else:
+            shortconv_kv_decode_mxfp8(d["k"], d["v"], mx.k_taps, mx.v_taps, mx.k_gamma,
+                                      mx.v_gamma, w.eps, mx.k_state, mx.v_state, d["sidx"],
+                                      d["slot"], mx.k_codes, mx.v_codes, mx.k_scales,
+                                      mx.v_scales)
+    torch.cuda.synchronize()
+    return plain, mx
+
+
+def _written_slots(w):
+    s = np.concatenate([st.slot_mapping for st in w.steps])
+    return s[(s >= 0) & (s < w.num_slots)]
+
+
+@pytest.mark.parametrize("H,D,W", [(2, 64, 4), (3, 128, 8), (1, 256, 2)])
+def test_fused_mx_equals_quantized_fp32_output(H, D, W):
+    spec = workloads.Spec(dtype="f32", H=H, D=D, W=W, seed=40 + W, prefill_lens=[37, 0, 5, 100],
+                          has_init=[1, 0, 1, 0], decode_ctx=[3, 50], pad_slot_every=13,
+                          outlier_p=0.02)
+    w = workloads.build(spec)
+    plain, mx = _fused_pair(w)
+    rows = _written_slots(w)
+    for cache, codes, scales in ((plain.k_cache, mx.k_codes, mx.k_scales),
+                                 (plain.v_cache, mx.v_codes, mx.v_scales)):
+        y32 = to_host(cache, "f32")[rows].astype(np.float64)
+        ec, es = oracle.mxfp8_quantize(y32)
+        assert np.array_equal(scales.cpu().numpy()[rows], es)
+        assert np.array_equal(codes.cpu().numpy()[rows], ec)
+        untouched = np.setdiff1d(np.arange(w.num_slots), rows)
+        assert (codes.cpu().numpy()[untouched] == 0xA5).all()
+        assert (scales.cpu().numpy()[untouched] == 0xA5).all()
+    for a, b in ((plain.k_state, mx.k_state), (plain.v_state, mx.v_state)):
+        assert np.array_equal(to_host(a, "f32"), to_host(b, "f32")), "conv state must not change"
+
+
+def test_fused_mx_bf16_within_one_step_of_oracle():
+    spec = workloads.Spec(dtype="bf16", H=8, D=128, W=4, seed=51, prefill_lens=[300, 17, 1000],
+                          has_init=[0, 1, 1], decode_ctx=[9, 70, 2], outlier_p=0.01)
+    w = workloads.build(spec)
+    plain, mx = _fused_pair(w)
+    from gpu_harness import oracle_steps
+    res = oracle_steps(w)
+    for name, codes_d, scales_d in (("K", mx.k_codes, mx.k_scales), ("V", mx.v_codes, mx.v_scales)):
+        codes = codes_d.cpu().numpy()
+        scales = scales_d.cpu().numpy()
+        for r in res:
+            ok = r.slots >= 0
+            y = (r.y_k if name == "K" else r.y_v)[ok]
+            ec, es = oracle.mxfp8_quantize(y)
+            gc, gs = codes[r.slots[ok]], scales[r.slots[ok]]
+            blocks = np.abs(y).reshape(*y.shape[:-1], -1, 32).max(-1)
+            near_pow2 = np.abs(np.log2(np.maximum(blocks, 1e-300)) -
+                               np.round(np.log2(np.maximum(blocks, 1e-300)))) < 1e-5
+            assert ((gs == es) | near_pow2).all(), f"{name}: scale differs off a 2^k boundary"
+            same = np.repeat(gs == es, 32, axis=-1)
+            gv, ev = oracle.e4m3_decode(gc), oracle.e4m3_decode(ec)
+            step = np.maximum(np.abs(ev) * 2.0 ** -3, 2.0 ** -9)
+            assert (np.abs(gv - ev)[same] <= step[same] * (1 + 1e-9)).all(), f"{name}: codes"
+            assert (gc == ec)[same].mean() > 0.99
+    for a, b in ((plain.k_state, mx.k_state), (plain.v_state, mx.v_state)):
+        assert np.array_equal(to_host(a, "bf16"), to_host(b, "bf16")), "conv state must not change"
+
+
+def test_mx_rejects_missing_scales():
+    from causal_short_convolution_amd import ShortConvError
+    w = workloads.build(workloads.Spec(dtype="bf16", H=8, D=128, W=4, seed=2, prefill_lens=[4],
+                                       has_init=[0]))
+    dw = DeviceWorkload(w, caches=False)
+    d = dw.steps[0]
+    codes = torch.zeros((w.num_slots, 8, 128), dtype=torch.uint8, device=DEV)
+    with pytest.raises(ShortConvError, match="scale"):
+        shortconv_kv_prefill_mxfp8(d["k"], d["v"], d["cu"], dw.k_taps, dw.v_taps, dw.k_gamma,
+                                   dw.v_gamma, w.eps, dw.k_state, dw.v_state, d["sidx"],
+                                   d["hinit"], d["slot"], codes, codes.clone(), None, None)
