@@ -41,6 +41,8 @@ KERNEL_SRC = os.path.join(ROOT, "causal_short_convolution_amd", "csrc", "kernels
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_varlen_bf16_traffic.md")
 WORKLOADS = {"tiny_ref": 1, "varlen_prefill": 2, "decode": 3, "long_prefill": 4, "mixed": 5}
 COPY_BYTES = 512 << 20          # calibration copy: 512 MiB read + 512 MiB written
+KERNELS = ("prefill_kernel", "decode_kernel", "verify_kernel", "commit_kernel",
+           "mx_quantize_kernel")
 
 
 def kernel_source_sha():
@@ -50,24 +52,53 @@ def kernel_source_sha():
 
 # ------------------------------------------------------------------------------------------------
 # Algorithmic bytes: what the step must move, with no halo re-reads and no metadata caching.
-# R = H * D * element bytes (one token row of K or V).
-#   prefill: per token read K and V rows, write K and V cache rows, read the int64 slot (4R + 8);
-#            per sequence read cu_seqlens, state_idx, has_init (9 B) and write 2 (W-1) state rows,
-#            plus 2 (W-1) state rows read when it resumes from a stored state; taps and gamma once.
-#   decode:  per token 2R new rows + 2 (W-1) R state read + 2 (W-1) R state written + 2R cache
+# R = H * D * element bytes (one token row of K or V); C = one cache row: R, or for MXFP8 rows
+# H * D code bytes + H * D / 32 scale bytes.
+#   prefill: per token read K and V rows, write K and V cache rows, read the int64 slot (2R + 2C
+#            + 8); per sequence read cu_seqlens, state_idx, has_init (9 B) and write 2 (W-1) state
+#            rows, plus 2 (W-1) state rows read when it resumes from a stored state; taps and
+#            gamma once.
+#   decode:  per token 2R new rows + 2 (W-1) R state read + 2 (W-1) R state written + 2C cache
 #            rows + 8 B slot + 4 B state index; taps and gamma once.
+#   verify:  as prefill resuming every sequence from its state, but instead of the state write,
+#            2 (W-1) R snapshot bytes per token; commit: per sequence cu_seqlens, accepted and
+#            state_idx (12 B) and, where it accepts a token, 2 (W-1) R snapshot read + 2 (W-1) R
+#            state written.
 # ------------------------------------------------------------------------------------------------
-def algorithmic_bytes(w, step):
+def cache_row_bytes(w, cache):
+    E = 4 if w.dtype == "f32" else 2
+    return w.H * w.D * E if cache == "io" else w.H * w.D + w.H * w.D // 32
+
+
+def algorithmic_bytes(w, step, cache="io"):
     E = 4 if w.dtype == "f32" else 2
     R = w.H * w.D * E
+    C = cache_row_bytes(w, cache)
     params = 2 * (w.W * w.H * w.D * 4 + w.D * 4)
     if step.kind == "prefill":
         T, N = step.tokens, step.num_seqs
         n_init = int(step.has_init.sum()) if w.W > 1 else 0
         state = 2 * (w.W - 1) * R * (N + n_init) if w.W > 1 else 0
-        return T * (4 * R + 8) + N * 9 + 4 + state + params
+        return T * (2 * R + 2 * C + 8) + N * 9 + 4 + state + params
     B = step.tokens
-    return B * (4 * R + 4 * (w.W - 1) * R + 12) + params
+    return B * (2 * R + 2 * C + 4 * (w.W - 1) * R + 12) + params
+
+
+def verify_bytes(w, accepted, max_tokens):
+    """(verify bytes, commit bytes) of one speculative step of workload w."""
+    import numpy as np
+    st = w.steps[0]
+    E = 4 if w.dtype == "f32" else 2
+    R = w.H * w.D * E
+    rows = 2 * (w.W - 1) * R
+    lens = np.diff(st.cu_seqlens.astype(np.int64))
+    N, T = st.num_seqs, st.tokens
+    params = 2 * (w.W * w.H * w.D * 4 + w.D * 4)
+    verify = (T * (4 * R + 8) + N * 8 + 4 + rows * N + rows * int(np.minimum(lens, max_tokens)
+                                                                  .sum()) + params)
+    m = np.minimum(np.minimum(accepted, lens), max_tokens)
+    commit = N * 12 + 4 + 2 * rows * int((m >= 1).sum())
+    return verify, commit
 
 
 def parse():
@@ -78,6 +109,10 @@ def parse():
     ap.add_argument("--workload", default="varlen_prefill", choices=sorted(WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the MXFP8-cache and speculative-verify measurements")
+    ap.add_argument("--only", default=None, choices=["main", "decode", "mxfp8", "verify"],
+                    help="run one measurement only (for profiling); prints no JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline sample")
@@ -90,10 +125,11 @@ def parse():
 # ------------------------------------------------------------------------------------------------
 # Device side
 # ------------------------------------------------------------------------------------------------
-def device_replicas(w, torch, n_rep, reseed=None):
-    """n_rep device copies of workload w (fresh buffers each). Replica r > 0 of a workload with
-    decode steps is drawn again with another seed (reseed(r)), so its decode slots differ and
-    writes never revisit a row; decode steps of all replicas share one cache pool."""
+def device_replicas(w, torch, n_rep, reseed=None, cache="io"):
+    """n_rep device copies of workload w (fresh buffers each). With reseed, replica r > 0 is
+    drawn again with another seed (reseed(r)), so its slots differ and writes never revisit a
+    row, and all replicas share one cache pool (decode-style pools are tens of GB). cache="io"
+    allocates I/O-dtype cache rows, "mxfp8" code and scale rows."""
     import numpy as np
     from causal_short_convolution_amd import _binding  # noqa: F401  (fails loudly if not built)
 
@@ -109,7 +145,6 @@ def device_replicas(w, torch, n_rep, reseed=None):
 
     shared = dict(k_taps=t(w.k_taps), v_taps=t(w.v_taps), k_gamma=t(w.k_gamma),
                   v_gamma=t(w.v_gamma), eps=w.eps)
-    has_decode = any(st.kind == "decode" for st in w.steps)
     reps = []
     for r in range(n_rep):
         wr = reseed(r) if (reseed is not None and r > 0) else w
@@ -126,38 +161,68 @@ def device_replicas(w, torch, n_rep, reseed=None):
         rep = {"steps": steps, "num_slots": wr.num_slots,
                "k_state": t(wr.k_state), "v_state": t(wr.v_state)}
         reps.append(rep)
-    if has_decode:  # one pool large enough for every replica's slots
-        ns = max(r["num_slots"] for r in reps)
-        kc = torch.empty((ns, w.H, w.D), dtype=dt, device=dev)
-        vc = torch.empty((ns, w.H, w.D), dtype=dt, device=dev)
+    def pool(ns):
+        if cache == "io":
+            return {"k_cache": torch.empty((ns, w.H, w.D), dtype=dt, device=dev),
+                    "v_cache": torch.empty((ns, w.H, w.D), dtype=dt, device=dev)}
+        u8 = torch.uint8
+        return {"k_cache": torch.empty((ns, w.H, w.D), dtype=u8, device=dev),
+                "v_cache": torch.empty((ns, w.H, w.D), dtype=u8, device=dev),
+                "k_scales": torch.empty((ns, w.H, w.D // 32), dtype=u8, device=dev),
+                "v_scales": torch.empty((ns, w.H, w.D // 32), dtype=u8, device=dev)}
+
+    if reseed is not None:  # one pool large enough for every replica's slots
+        shared_pool = pool(max(r["num_slots"] for r in reps))
         for r in reps:
-            r["k_cache"], r["v_cache"] = kc, vc
+            r.update(shared_pool)
     else:
         for r in reps:
-            r["k_cache"] = torch.empty((r["num_slots"], w.H, w.D), dtype=dt, device=dev)
-            r["v_cache"] = torch.empty((r["num_slots"], w.H, w.D), dtype=dt, device=dev)
+            r.update(pool(r["num_slots"]))
     return reps
 
 
-def launcher(w, rep):
+def launcher(w, rep, cache="io"):
     """One bench step: every call of the workload, in order, on the current stream."""
-    from causal_short_convolution_amd import shortconv_kv_decode, shortconv_kv_prefill
+    import causal_short_convolution_amd as sc
     calls = []
+    mx = cache == "mxfp8"
     for d in rep["steps"]:
+        sc_args = (d["k_taps"], d["v_taps"], d["k_gamma"], d["v_gamma"], d["eps"],
+                   rep["k_state"], rep["v_state"], d["sidx"])
+        out = (rep["k_cache"], rep["v_cache"]) + ((rep["k_scales"], rep["v_scales"]) if mx else ())
         if d["kind"] == "prefill":
-            calls.append(lambda d=d: shortconv_kv_prefill(
-                d["k"], d["v"], d["cu"], d["k_taps"], d["v_taps"], d["k_gamma"], d["v_gamma"],
-                d["eps"], rep["k_state"], rep["v_state"], d["sidx"], d["hinit"], d["slot"],
-                rep["k_cache"], rep["v_cache"]))
+            fn = sc.shortconv_kv_prefill_mxfp8 if mx else sc.shortconv_kv_prefill
+            calls.append(lambda d=d, fn=fn, a=sc_args, o=out: fn(
+                d["k"], d["v"], d["cu"], *a, d["hinit"], d["slot"], *o))
         else:
-            calls.append(lambda d=d: shortconv_kv_decode(
-                d["k"], d["v"], d["k_taps"], d["v_taps"], d["k_gamma"], d["v_gamma"], d["eps"],
-                rep["k_state"], rep["v_state"], d["sidx"], d["slot"], rep["k_cache"],
-                rep["v_cache"]))
+            fn = sc.shortconv_kv_decode_mxfp8 if mx else sc.shortconv_kv_decode
+            calls.append(lambda d=d, fn=fn, a=sc_args, o=out: fn(d["k"], d["v"], *a, d["slot"],
+                                                                 *o))
 
     def step():
         for c in calls:
             c()
+    return step
+
+
+def verify_launcher(w, rep, accepted, max_tokens, torch):
+    """One speculative step: verify the candidate runs (cache rows + per-token snapshots), then
+    commit the accepted prefix of each sequence into the state pools."""
+    import causal_short_convolution_amd as sc
+    d = rep["steps"][0]
+    shape = (w.steps[0].num_seqs, max_tokens, w.W - 1, w.H, w.D)
+    k_snap = torch.empty(shape, dtype=d["k"].dtype, device=d["k"].device)
+    v_snap = torch.empty_like(k_snap)
+    acc = torch.from_numpy(accepted).to(d["k"].device)
+    T = d["k"].shape[0]
+
+    def step():
+        sc.shortconv_kv_verify(d["k"], d["v"], d["cu"], d["k_taps"], d["v_taps"], d["k_gamma"],
+                               d["v_gamma"], d["eps"], rep["k_state"], rep["v_state"], d["sidx"],
+                               k_snap, v_snap, d["slot"], rep["k_cache"], rep["v_cache"])
+        sc.shortconv_state_commit(k_snap, v_snap, d["cu"], T, acc, rep["k_state"],
+                                  rep["v_state"], d["sidx"], width=w.W, num_heads=w.H,
+                                  head_dim=w.D)
     return step
 
 
@@ -196,15 +261,17 @@ def time_steps(torch, fns, steps, warmup, graph=True):
     return wall, start.elapsed_time(end)
 
 
-def measure(torch, w, steps, warmup, reseed=None, graph=True):
-    alg = sum(algorithmic_bytes(w, st) for st in w.steps)
+def measure(torch, w, steps, warmup, reseed=None, graph=True, cache="io"):
+    alg = sum(algorithmic_bytes(w, st, cache) for st in w.steps)
     tokens = w.tokens
     n_rep = max(2, math.ceil(2 * MALL_BYTES / alg) + 1)
-    reps = device_replicas(w, torch, n_rep, reseed)
-    fns = [launcher(w, r) for r in reps]
+    reps = device_replicas(w, torch, n_rep, reseed, cache)
+    fns = [launcher(w, r, cache) for r in reps]
     wall, dev_ms = time_steps(torch, fns, steps, warmup, graph)
+    del reps, fns
     per_step_ms = dev_ms / steps
     return {
+        "cache": cache,
         "tokens_per_step": tokens,
         "launches_per_step": len(w.steps),
         "replicas": n_rep,
@@ -216,6 +283,31 @@ def measure(torch, w, steps, warmup, reseed=None, graph=True):
         "algorithmic_bytes": alg,
         "achieved_GBps": alg / (per_step_ms * 1e-3) / 1e9,
     }
+
+
+def measure_verify(torch, steps, warmup, seed, graph=True):
+    """Speculative verify + commit at the decode shape (workloads.spec_verify)."""
+    import workloads
+    w, accepted = workloads.spec_verify(seed)
+    mt = workloads.SPEC_TOKENS
+    vb, cb = verify_bytes(w, accepted, mt)
+    n_rep = max(2, math.ceil(2 * MALL_BYTES / (vb + cb)) + 1)
+    draws = {0: (w, accepted)}
+
+    def reseed(r):
+        draws[r] = workloads.spec_verify(seed + 1000 * r)
+        return draws[r][0]
+
+    reps = device_replicas(w, torch, n_rep, reseed)
+    fns = [verify_launcher(draws[i][0], r, draws[i][1], mt, torch) for i, r in enumerate(reps)]
+    wall, dev_ms = time_steps(torch, fns, steps, warmup, graph)
+    del reps, fns
+    per_ms = dev_ms / steps
+    return {"workload": w.name, "recipe": w.recipe, "tokens_per_step": w.tokens,
+            "launches_per_step": 2, "replicas": n_rep, "ms_per_step": 1e3 * wall / steps,
+            "tokens_per_s": w.tokens * steps / wall, "kernel_us_mean": 1e3 * per_ms,
+            "algorithmic_bytes": vb + cb, "verify_bytes": vb, "commit_bytes": cb,
+            "achieved_GBps": (vb + cb) / (per_ms * 1e-3) / 1e9}
 
 
 def copy_ceiling(torch, bytes_moved, steps, warmup):
@@ -297,6 +389,10 @@ def summarize_profile(dirs):
     the fused kernels from FETCH_SIZE / WRITE_SIZE passes, each scaled by what the same counter
     reads for the calibration copy (--calibrate-copy: COPY_BYTES read and COPY_BYTES written)."""
     import csv
+
+    def short(name):
+        return name.replace("sc::(anonymous namespace)::", "").replace(
+            "(anonymous namespace)::", "").replace("void ", "")
     out = []
     per = {}  # (kernel, counter) -> values per dispatch
     for d in dirs:
@@ -304,17 +400,30 @@ def summarize_profile(dirs):
             out.append(f"kernel stats ({os.path.relpath(path, ROOT)}):")
             with open(path) as f:
                 for row in csv.DictReader(f):
-                    out.append(f"  {row['Name'][:100]:100s} calls={row['Calls']:>5s} "
+                    out.append(f"  {short(row['Name'])[:60]:60s} calls={row['Calls']:>5s} "
                                f"avg_ns={float(row['AverageNs']):10.1f} "
                                f"min_ns={row['MinNs']:>8s} max_ns={row['MaxNs']:>8s}")
+        for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+            durs = {}
+            with open(path) as f:
+                for row in csv.DictReader(f):
+                    ns = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+                    durs.setdefault(short(row["Kernel_Name"]), []).append(ns)
+            out.append(f"per-dispatch durations ({os.path.relpath(path, ROOT)}):")
+            for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+                v = sorted(v)
+
+                def q(f, v=v):
+                    return v[min(len(v) - 1, int(f * len(v)))]
+                out.append(f"  {name[:60]:60s} n={len(v):>5d} mean_ns={sum(v) / len(v):10.1f} "
+                           f"p10_ns={q(0.1):>8d} median_ns={q(0.5):>8d} p90_ns={q(0.9):>8d}")
         for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"),
                                      recursive=True)):
             with open(path) as f:
                 for row in csv.DictReader(f):
-                    name = row["Kernel_Name"]
-                    kind = ("prefill_kernel" if "prefill_kernel" in name else
-                            "decode_kernel" if "decode_kernel" in name else
-                            "copy" if "copyBuffer" in name else None)
+                    name = short(row["Kernel_Name"])
+                    kind = ("copy" if "copyBuffer" in name else name.split("(")[0]
+                            if any(k in name for k in KERNELS) else None)
                     if kind:
                         per.setdefault((kind, row["Counter_Name"]), []).append(
                             float(row["Counter_Value"]))
@@ -326,7 +435,7 @@ def summarize_profile(dirs):
             factors[ctr] = known_kib / (sum(copies) / len(copies))
             out.append(f"calibration copy {ctr}: {sum(copies) / len(copies):.1f} KiB per dispatch "
                        f"for {known_kib:.0f} KiB moved -> factor {factors[ctr]:.4f}")
-    for kind in ("prefill_kernel", "decode_kernel"):
+    for kind in sorted({k for k, _ in per if k != "copy"}):
         vals = {c: per.get((kind, c)) for c in ("FETCH_SIZE", "WRITE_SIZE")}
         if all(vals.values()) and len(factors) == 2:
             f_kib = sum(vals["FETCH_SIZE"]) / len(vals["FETCH_SIZE"])
@@ -361,17 +470,41 @@ def main():
     n = WORKLOADS[args.workload]
     w = workloads.config(n, seed=args.seed)
     has_decode = any(st.kind == "decode" for st in w.steps)
-    main_m = measure(torch, w, args.steps, args.warmup,
-                     reseed=(lambda r: workloads.config(n, seed=args.seed + 1000 * r))
-                     if has_decode else None, graph=not args.eager)
+    reseed_main = ((lambda r: workloads.config(n, seed=args.seed + 1000 * r))
+                   if has_decode else None)
+    graph = not args.eager
+    if args.only:
+        print(f"bench.py: measuring {args.only} only", flush=True)
+        if args.only == "main":
+            m = measure(torch, w, args.steps, args.warmup, reseed_main, graph)
+        elif args.only == "mxfp8":
+            m = measure(torch, w, args.steps, args.warmup, reseed_main, graph, cache="mxfp8")
+        elif args.only == "decode":
+            m = measure(torch, workloads.config(3, seed=args.seed), args.steps, args.warmup,
+                        lambda r: workloads.config(3, seed=args.seed + 1000 * r), graph)
+        else:
+            m = measure_verify(torch, args.steps, args.warmup, args.seed, graph)
+        print(f"bench.py: {args.only}: {m['kernel_us_mean']:.2f} us per step, "
+              f"{m['achieved_GBps']:.0f} GB/s", flush=True)
+        return 0
+    main_m = measure(torch, w, args.steps, args.warmup, reseed_main, graph)
     extra = {}
     if not args.no_decode and args.workload != "decode":
         wd = workloads.config(3, seed=args.seed)
         dm = measure(torch, wd, args.steps, args.warmup,
                      reseed=lambda r: workloads.config(3, seed=args.seed + 1000 * r),
-                     graph=not args.eager)
+                     graph=graph)
         extra["decode"] = {"workload": "decode", "recipe": wd.recipe, **_round(dm),
                            "frac_of_hbm_peak": dm["achieved_GBps"] / HBM_PEAK_GBPS}
+    if not args.no_extras:
+        mm = measure(torch, w, args.steps, args.warmup, reseed_main, graph, cache="mxfp8")
+        extra["mxfp8_cache"] = {"workload": w.name, **_round(mm),
+                                "frac_of_hbm_peak": mm["achieved_GBps"] / HBM_PEAK_GBPS,
+                                "vs_io_cache_time": mm["kernel_us_mean"] /
+                                main_m["kernel_us_mean"]}
+        vm = measure_verify(torch, args.steps, args.warmup, args.seed, graph)
+        extra["spec_verify"] = {**_round(vm),
+                                "frac_of_hbm_peak": vm["achieved_GBps"] / HBM_PEAK_GBPS}
     if args.calibrate_copy:
         calibration_copy(torch)
     ceil = copy_ceiling(torch, main_m["algorithmic_bytes"], args.steps, args.warmup)

@@ -234,21 +234,18 @@ struct PlainSink {
     }
 };
 
-// OCP FP8 E4M3 code of v (finite): nearest value, ties to even, saturating at +-448. Exact:
-// the rounding works on the binary32 pattern (normal range) or on v * 2^9, an exact scaling
-// (subnormal range, steps of 2^-9).
-__device__ inline uint32_t e4m3_code(float v) {
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t ua = u & 0x7fffffffu;
-    // normal: keep 3 fraction bits, round the 20 below to nearest even; the exponent rebias
-    // (127 - 7) moves to the code's exponent field; a carry out of the fraction is correct.
-    uint32_t n = (ua + 0x7ffffu + ((ua >> 20) & 1u)) >> 20;
-    n = n - (120u << 3);
-    n = n > 0x7eu ? 0x7eu : n;  // beyond 448 (including rounding up to 480): saturate
-    const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(ua) * 512.0f);
-    const uint32_t code = ua >= 0x3c800000u ? n : sub;  // 0x3c800000 = 2^-6, the smallest normal
-    return code | sign;
+// OCP FP8 E4M3 codes of four finite values, byte b = code of v[b]: nearest value, ties to even,
+// saturating at +-448. gfx950's packed conversion rounds to nearest even into the OCP format but
+// does not saturate, so the values are clamped to the largest finite code first.
+__device__ inline uint32_t e4m3x4(float v0, float v1, float v2, float v3) {
+    constexpr float kMax = 448.0f;
+    v0 = __builtin_amdgcn_fmed3f(v0, -kMax, kMax);
+    v1 = __builtin_amdgcn_fmed3f(v1, -kMax, kMax);
+    v2 = __builtin_amdgcn_fmed3f(v2, -kMax, kMax);
+    v3 = __builtin_amdgcn_fmed3f(v3, -kMax, kMax);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
+    return (uint32_t)w;
 }
 
 // MXFP8 rows: 32-element blocks along head_dim share one E8M0 scale 2^e with
@@ -285,13 +282,10 @@ struct MxSink {
         e = e < -127 ? -127 : (e > 127 ? 127 : e);
         uint32_t packed[VEC / 4];
 #pragma unroll
-        for (int q = 0; q < VEC / 4; ++q) {
-            uint32_t w = 0;
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                w |= e4m3_code(__builtin_ldexpf(o[4 * q + b], -e)) << (8 * b);
-            packed[q] = w;
-        }
+        for (int q = 0; q < VEC / 4; ++q)
+            packed[q] = e4m3x4(__builtin_ldexpf(o[4 * q], -e), __builtin_ldexpf(o[4 * q + 1], -e),
+                               __builtin_ldexpf(o[4 * q + 2], -e),
+                               __builtin_ldexpf(o[4 * q + 3], -e));
         if (!(active && slot >= 0 && slot < num_slots)) return;
         char* row = codes + slot * row_elems + code_off;
         if (VEC == 8) {

@@ -21,6 +21,7 @@ import numpy as np
 # stream ids (the third SeedSequence word)
 _S_LENS, _S_K, _S_V, _S_KTAP, _S_VTAP, _S_KG, _S_VG, _S_KST, _S_VST = range(9)
 _S_BLOCKS, _S_SIDX, _S_DEC_CTX, _S_START, _S_KOUT, _S_VOUT, _S_DK, _S_DV, _S_PAD = range(9, 18)
+_S_ACCEPT = 18
 
 # Finite bit patterns that untouched cache rows keep (checked bit for bit after a step).
 SENTINEL = {"f32": np.uint32(0x5A5A5A5A), "bf16": np.uint16(0x5A5A)}
@@ -275,3 +276,28 @@ RECIPES = {
     5: "64 chunks x 2048 tokens resuming at 2048*U{1..15} from state~N(0,1) + 512 decodes "
        "(context U{1..32768}), H=16, D=128, W=4, bf16; paged cache, block 16, permuted tables",
 }
+
+
+# ---------------------------------------------------------------------------------------------
+# Speculative verification at the decode shape. The pages give no shapes for it; this takes the
+# decode workload's sequences, each verifying a run of SPEC_TOKENS candidate tokens (the first
+# being the token sampled last step), and draws how many of them the target model accepts.
+# ---------------------------------------------------------------------------------------------
+SPEC_TOKENS = 4
+SPEC_RECIPE = ("256 sequences x 4 candidate tokens, H=8, D=128, W=4, bf16; every sequence resumes "
+               "from its stored state (rows~N(0,1)); context U{5..32768} after the run; paged "
+               "cache, block 64, permuted block tables; accepted count U{0..4} per sequence")
+
+
+def spec_verify(seed: int = 0):
+    """(workload, accepted): one verification call of SPEC_TOKENS tokens per sequence and the
+    number of them accepted (int32 [256]), for the verify + state-commit pair."""
+    ctx = rng(seed, 6, _S_DEC_CTX).integers(SPEC_TOKENS + 1, 32768, size=256, endpoint=True)
+    spec = Spec(name="spec_verify", dtype="bf16", H=8, D=128, W=4, seed=seed, tag=6,
+                prefill_lens=[SPEC_TOKENS] * 256, prefill_start=(ctx - SPEC_TOKENS).tolist(),
+                has_init=[1] * 256, block_size=64)
+    w = build(spec)
+    w.recipe = SPEC_RECIPE
+    accepted = rng(seed, 6, _S_ACCEPT).integers(0, SPEC_TOKENS, size=256,
+                                                endpoint=True).astype(np.int32)
+    return w, accepted
