@@ -20,10 +20,14 @@ PROBE_LIB = os.path.join(HERE, "libscprobe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "copy_probe.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+# -ffp-contract=off: every fused multiply-add is written out, so prefill and decode round alike.
+# -packed-fp32-ops: no packed fp32 instructions are generated.
+# -fno-slp-vectorize: the kernels' arrays are per-lane registers; grouping them into vectors only
+#   adds shuffles and, for some widths, doubles register use (bf16 prefill at width 4 spills).
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
     "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-fno-slp-vectorize", "-Wall", "-Wno-unused-function",
 ]
 
 

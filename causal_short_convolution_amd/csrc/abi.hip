@@ -125,7 +125,7 @@ int prefill_impl(const char* fn, const void* k, const void* v, int64_t k_tok_str
     a.has_init = has_initial_state;
     a.tokens = total_tokens;
     a.num_seqs = num_seqs;
-    const int bt = sc::prefill_tile_tokens(dtype, head_dim, width);
+    const int bt = sc::prefill_tile_tokens(dtype, head_dim, width, mx);
     const int64_t tiles = total_tokens / bt + num_seqs;  // upper bound, see kernels.hip
     if (tiles * ((2 * (int64_t)a.lanes_per_tensor + 63) / 64) > INT32_MAX)
         return fail(SC_ERR_UNSUPPORTED, "%s: problem too large for one launch", fn);

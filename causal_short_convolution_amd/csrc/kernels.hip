@@ -14,18 +14,23 @@
 // contiguous 16-byte-per-lane access. Lanes [0, lanes_per_tensor) work on K and the rest on V.
 //
 // Prefill tiles: a workgroup covers one 64-lane (1 KiB) column slice of the K|V rows over a tile of
-// 4 * BT consecutive tokens of ONE sequence; each of its 4 wavefronts walks BT of those tokens,
-// keeping the sliding window in registers (each input row is loaded once and reused by the W
-// outputs that read it). Wave w > 0 gets its W-1 halo rows from wave w-1 through LDS (an
-// LDS-staged halo, so a row is fetched from HBM once); wave 0 reads the tail of the previous tile
-// of the same sequence, or the sequence's conv state / zeros for its first tile. All 4 waves use
-// the same taps and gamma, so 3 of 4 parameter loads hit in L1. Tiles never straddle sequences:
+// 4 * BT consecutive tokens of ONE sequence (BT = 8 for W <= 4, 16 for wider windows, whose
+// halo is a larger share of a short span); each of its 4 wavefronts walks BT of those tokens,
+// keeping the window in registers (each input row is loaded once and reused by the W outputs
+// that read it). Wave w > 0 gets its W-1 halo rows from wave w-1 through LDS (an LDS-staged
+// halo, so a row is fetched from HBM once); wave 0 reads the tail of the previous tile of the
+// same sequence, or the sequence's conv state / zeros for its first tile. All 4 waves use the
+// same taps and gamma, so 3 of 4 parameter loads hit in L1. Tiles never straddle sequences:
 // sequence s owns tiles [P(s), P(s) + max(1, ceil(L_s / (4*BT)))) with P(s) = floor(cu[s] /
 // (4*BT)) + s. P is strictly increasing and P(s) + max(1, ceil(L_s/(4*BT))) <= P(s+1), so a
 // workgroup finds its sequence by a wave-parallel search over cu_seqlens (one vector load per 64x
-// narrowing) with no host-side scan; at most one tile per sequence is empty. Loads are issued in
-// the order their data is needed, since vector loads return in order: taps and gamma, halo, the
-// rows the next wave needs, then the other rows.
+// narrowing) with no host-side scan; at most one tile per sequence is empty.
+//
+// Memory order within a wave: after the search, every load of the span goes out back to back
+// (parameters, halo, the rows the next wave needs first, the other rows, the span's slots as one
+// vector load), with no branch between them; then the tokens are computed in order, each
+// waiting only for its own row (see the token loop for why the first stores wait until half
+// the span is computed).
 //
 // Conv-state ownership: only the first wave of a sequence's first tile reads the old state (its
 // halo), so that wave also writes the new state (the sequence's last W-1 raw rows, taken from the
@@ -46,16 +51,43 @@ namespace {
 
 constexpr int kBlock = 256;  // threads per workgroup (4 wavefronts)
 
-// Build-time tuning knobs (defaults chosen by measurement on MI355X).
-#ifndef SC_PREFILL_TILE
-#define SC_PREFILL_TILE 16       // tokens per wave span in prefill, width <= 4
+// Build-time tuning knobs (defaults chosen by measurement on MI355X): tokens per wave span in
+// prefill and the minimum resident waves per SIMD that the register budget must allow, for
+// narrow (W <= 4) and wide windows, with plain and with MXFP8 cache rows.
+#ifndef SC_BT_NARROW
+#define SC_BT_NARROW 8
 #endif
-#ifndef SC_PREFILL_TILE_WIDE
-#define SC_PREFILL_TILE_WIDE 16  // tokens per wave span in prefill, width > 4
+#ifndef SC_WAVES_NARROW
+#define SC_WAVES_NARROW 4
 #endif
-#ifndef SC_PREFILL_MIN_WAVES
-#define SC_PREFILL_MIN_WAVES 2   // minimum resident waves per SIMD the register budget must allow
+#ifndef SC_BT_NARROW_MX
+#define SC_BT_NARROW_MX 8
 #endif
+#ifndef SC_WAVES_NARROW_MX
+#define SC_WAVES_NARROW_MX 3
+#endif
+#ifndef SC_BT_WIDE
+#define SC_BT_WIDE 16
+#endif
+#ifndef SC_WAVES_WIDE
+#define SC_WAVES_WIDE 2
+#endif
+#ifndef SC_BT_WIDE_MX
+#define SC_BT_WIDE_MX 16
+#endif
+#ifndef SC_WAVES_WIDE_MX
+#define SC_WAVES_WIDE_MX 2
+#endif
+
+template <int W, bool MX>
+constexpr int span_tokens() {
+    return W <= 4 ? (MX ? SC_BT_NARROW_MX : SC_BT_NARROW) : (MX ? SC_BT_WIDE_MX : SC_BT_WIDE);
+}
+template <int W, bool MX>
+constexpr int span_min_waves() {
+    return W <= 4 ? (MX ? SC_WAVES_NARROW_MX : SC_WAVES_NARROW)
+                  : (MX ? SC_WAVES_WIDE_MX : SC_WAVES_WIDE);
+}
 
 // ------------------------------------------------------------------------------------------------
 // Element types. A "packet" is the 16 bytes one lane moves: uint4.
@@ -120,12 +152,36 @@ __device__ inline void strow(char* base, uint32_t lane_off, const uint4& v) {
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(base + lane_off));
 }
 
+// Waits until every vector memory access this wave has issued is complete (s_waitcnt vmcnt(0),
+// other counters unconstrained). On gfx9 stores count in vmcnt too: where a span's row loads are
+// followed by conditional cache stores, the compiler cannot tell how many operations follow a
+// row and waits for all of them, stores included, before each row. One explicit wait for the
+// rows before the loop leaves nothing in flight that a row could be waiting on.
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Values that are the same in every lane, moved to scalar registers so that the compiler uses
 // scalar loads for per-token metadata and scalar base addresses for the row accesses.
 __device__ inline int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ inline int64_t uniform(int64_t v) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Per-lane choice between the K and the V member of a pair of kernel arguments. Both members are
+// read as scalars and the lane selects; indexing the pair with the lane's tensor would instead be
+// a vector load from the argument segment, and every address derived from it would wait for it.
+template <class P>
+__device__ inline P pick(const P (&pair)[2], int tensor) {
+    const P k = pair[0];
+    const P v = pair[1];
+    return tensor ? v : k;
+}
+
+// Lane i's value of v, as a wave-uniform (scalar) value.
+__device__ inline int64_t lane_value(int64_t v, int i) {
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, i);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), i);
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
@@ -188,19 +244,22 @@ __device__ inline void load_params(const float* taps, const float* gamma, int he
     }
 }
 
-// The row math of one output row slice: window win[0..W-1] (win[W-1] = current token); o gets the
-// normalized values in fp32, before the one rounding to the cache format.
+// The row math of one output row slice: window row k (k = W-1 is the current token) is
+// win[(off + k) % W], off being a compile-time constant after unrolling; o gets the normalized
+// values in fp32, before the one rounding to the cache format.
 template <class E, int W, int LPH>
-__device__ inline void fused_row(const float (&win)[W][E::VEC], const LaneParams<E, W>& p,
-                                 float eps, float inv_d, float (&o)[E::VEC]) {
+__device__ inline void fused_row(const float (&win)[W][E::VEC], int off,
+                                 const LaneParams<E, W>& p, float eps, float inv_d,
+                                 float (&o)[E::VEC]) {
     constexpr int VEC = E::VEC;
     float c[VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) c[v] = p.tap[0][v] * win[0][v];
+    for (int v = 0; v < VEC; ++v) c[v] = p.tap[0][v] * win[off % W][v];
 #pragma unroll
     for (int k = 1; k < W; ++k)
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) c[v] = __builtin_fmaf(p.tap[k][v], win[k][v], c[v]);
+        for (int v = 0; v < VEC; ++v)
+            c[v] = __builtin_fmaf(p.tap[k][v], win[(off + k) % W][v], c[v]);
     float ss = 0.0f;
 #pragma unroll
     for (int v = 0; v < VEC; ++v) ss = __builtin_fmaf(c[v], c[v], ss);
@@ -224,13 +283,19 @@ struct PlainSink {
     uint32_t lane_off;
     int64_t num_slots;
     __device__ PlainSink(const StepArgs& a, int tensor, int h, int d0, int D)
-        : cache(static_cast<char*>(a.cache[tensor])),
+        : cache(static_cast<char*>(pick(a.cache, tensor))),
           row_bytes((int64_t)a.heads * D * E::BYTES),
           lane_off((uint32_t)(((int64_t)h * D + d0) * E::BYTES)),
           num_slots(a.num_slots) {}
-    __device__ void put(int64_t slot, bool active, const float (&o)[E::VEC]) const {
-        const uint4 out = E::narrow(o);
+    // A row slice in its stored form, and its store (skipped for an idle lane or a slot outside
+    // the pool).
+    using Enc = uint4;
+    __device__ Enc encode(const float (&o)[E::VEC]) const { return E::narrow(o); }
+    __device__ void write(int64_t slot, bool active, const Enc& out) const {
         if (active && slot >= 0 && slot < num_slots) strow(cache + slot * row_bytes, lane_off, out);
+    }
+    __device__ void put(int64_t slot, bool active, const float (&o)[E::VEC]) const {
+        write(slot, active, encode(o));
     }
 };
 
@@ -264,40 +329,51 @@ struct MxSink {
     bool scale_lane;
     int64_t num_slots;
     __device__ MxSink(const StepArgs& a, int tensor, int h, int d0, int D)
-        : codes(static_cast<char*>(a.cache[tensor])),
-          scales(static_cast<char*>(a.scales[tensor])),
+        : codes(static_cast<char*>(pick(a.cache, tensor))),
+          scales(static_cast<char*>(pick(a.scales, tensor))),
           row_elems((int64_t)a.heads * D),
           code_off((uint32_t)((int64_t)h * D + d0)),
           scale_off((uint32_t)(((int64_t)h * D + d0) / 32)),
           scale_lane(d0 % 32 == 0),
           num_slots(a.num_slots) {}
-    __device__ void put(int64_t slot, bool active, const float (&o)[VEC]) const {
+    struct Enc {
+        uint32_t packed[VEC / 4];  // the VEC codes, 4 per word
+        int e;                     // the block's scale exponent
+    };
+    __device__ Enc encode(const float (&o)[VEC]) const {
         float amax = 0.0f;
 #pragma unroll
         for (int v = 0; v < VEC; ++v) amax = __builtin_fmaxf(amax, __builtin_fabsf(o[v]));
         amax = __builtin_fmaxf(amax, dpp<kQuadXor1>(amax));
         amax = __builtin_fmaxf(amax, dpp<kQuadXor2>(amax));
         if (LPB == 8) amax = __builtin_fmaxf(amax, dpp<kRowHalfMirror>(amax));
+        Enc r;
         int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 1 - 8 : -127;
         e = e < -127 ? -127 : (e > 127 ? 127 : e);
-        uint32_t packed[VEC / 4];
+        r.e = e;
 #pragma unroll
         for (int q = 0; q < VEC / 4; ++q)
-            packed[q] = e4m3x4(__builtin_ldexpf(o[4 * q], -e), __builtin_ldexpf(o[4 * q + 1], -e),
-                               __builtin_ldexpf(o[4 * q + 2], -e),
-                               __builtin_ldexpf(o[4 * q + 3], -e));
+            r.packed[q] = e4m3x4(__builtin_ldexpf(o[4 * q], -e), __builtin_ldexpf(o[4 * q + 1], -e),
+                                 __builtin_ldexpf(o[4 * q + 2], -e),
+                                 __builtin_ldexpf(o[4 * q + 3], -e));
+        return r;
+    }
+    __device__ void write(int64_t slot, bool active, const Enc& enc) const {
         if (!(active && slot >= 0 && slot < num_slots)) return;
         char* row = codes + slot * row_elems + code_off;
         if (VEC == 8) {
             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-            const u32x2 w = {packed[0], packed[VEC / 4 - 1]};
+            const u32x2 w = {enc.packed[0], enc.packed[VEC / 4 - 1]};
             __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(row));
         } else {
-            __builtin_nontemporal_store(packed[0], reinterpret_cast<uint32_t*>(row));
+            __builtin_nontemporal_store(enc.packed[0], reinterpret_cast<uint32_t*>(row));
         }
         if (scale_lane)
             *reinterpret_cast<uint8_t*>(scales + slot * (row_elems / 32) + scale_off) =
-                (uint8_t)(e + 127);
+                (uint8_t)(enc.e + 127);
+    }
+    __device__ void put(int64_t slot, bool active, const float (&o)[VEC]) const {
+        write(slot, active, encode(o));
     }
 };
 
@@ -341,7 +417,7 @@ __device__ inline int find_tile_seq(const int32_t* cu, int n, int64_t T, int64_t
 }
 
 template <class E, int D, int W, int BT, bool MX>
-__global__ void __launch_bounds__(kBlock, SC_PREFILL_MIN_WAVES) prefill_kernel(StepArgs a) {
+__global__ void __launch_bounds__(kBlock, (span_min_waves<W, MX>())) prefill_kernel(StepArgs a) {
     constexpr int VEC = E::VEC;
     constexpr int LPH = D / VEC;
     constexpr int R = W - 1;
@@ -350,6 +426,7 @@ __global__ void __launch_bounds__(kBlock, SC_PREFILL_MIN_WAVES) prefill_kernel(S
     // A wave's halo is the tail of the previous wave's span, and the tile holding a sequence's
     // first token holds every position that reads the old state.
     static_assert(BT >= R, "a wave's span must cover the conv halo");
+    static_assert(BT <= 64, "a wave loads one slot per lane");
     // Tail rows that wave w hands to wave w+1 (an LDS-staged halo: HBM is read once per row).
     __shared__ uint4 handoff[NW - 1][R > 0 ? R : 1][64];
 
@@ -361,7 +438,8 @@ __global__ void __launch_bounds__(kBlock, SC_PREFILL_MIN_WAVES) prefill_kernel(S
     const int tile = blockIdx.x / slices;
     const int slice = blockIdx.x - tile * slices;
     const int lane = slice * 64 + wl;
-    const bool active = lane < 2 * a.lanes_per_tensor;  // idle lanes load lane 0's column, store nothing
+    // idle lanes load lane 0's column and store nothing
+    const bool active = lane < 2 * a.lanes_per_tensor;
     const int ln = active ? lane : 0;
     const int tensor = ln >= a.lanes_per_tensor;
     const int c = ln - tensor * a.lanes_per_tensor;
@@ -379,10 +457,10 @@ __global__ void __launch_bounds__(kBlock, SC_PREFILL_MIN_WAVES) prefill_kernel(S
     const int64_t ntiles = L > 0 ? (L + BB - 1) / BB : 1;
     if (j < 0 || j >= ntiles) return;  // the whole workgroup leaves together
 
-    const char* x = static_cast<const char*>(a.x[tensor]);
-    const int64_t stride_bytes = a.x_stride[tensor] * E::BYTES;
+    const char* x = static_cast<const char*>(pick(a.x, tensor));
+    const int64_t stride_bytes = pick(a.x_stride, tensor) * E::BYTES;
     const typename SinkFor<E, MX>::type sink(a, tensor, h, d0, D);
-    char* state = static_cast<char*>(a.state[tensor]);
+    char* state = static_cast<char*>(pick(a.state, tensor));
     const int64_t row_bytes = (int64_t)a.heads * D * E::BYTES;
     const uint32_t lane_off = (uint32_t)(((int64_t)h * D + d0) * E::BYTES);
 
@@ -392,13 +470,6 @@ __global__ void __launch_bounds__(kBlock, SC_PREFILL_MIN_WAVES) prefill_kernel(S
     const int n = rem <= 0 ? 0 : (rem < BT ? (int)rem : BT);
     const char* xb = x + t0 * stride_bytes;
 
-    // Loads in the order their data is needed (vector loads return in order): taps and gamma
-    // (cache hits), the first wave's halo, then the rows.
-    LaneParams<E, W> p;
-    load_params<E, W>(a.taps[tensor], a.gamma[tensor], a.heads, D, h, d0, p);
-
-    // The first wave of a tile reads its halo itself: the previous tile's last rows, or (for the
-    // sequence's first tile) the stored state or zeros.
     int32_t idx = -1;
     bool slot_ok = false, read_state = false;
     if (j == 0) {
@@ -406,63 +477,103 @@ __global__ void __launch_bounds__(kBlock, SC_PREFILL_MIN_WAVES) prefill_kernel(S
         slot_ok = R > 0 && state != nullptr && idx >= 0 && idx < a.num_state_slots;
         read_state = slot_ok && (a.has_init ? a.has_init[s] != 0 : true);
     }
-    const char* state_row = state + (int64_t)idx * R * row_bytes;  // used only when slot_ok
+
+    // Every load of a span goes out back to back (vector loads return in order), with no branch
+    // between them that could leave the compiler unsure how many are in flight: taps and gamma
+    // (cache hits), the first wave's halo, the rows the next wave needs, the other rows, and the
+    // span's cache slots. A wave whose span starts past its sequence's end loads nothing.
+    const bool has_rows = n > 0;
+    const bool first_span = j == 0 && w == 0;
+    LaneParams<E, W> p;
     uint4 halo[R > 0 ? R : 1];
-    if (w == 0) {
-#pragma unroll
-        for (int k = 0; k < R; ++k) {
-            halo[k] = make_uint4(0, 0, 0, 0);
-            if (j > 0)
-                halo[k] = ldrow(x + (t0 - R + k) * stride_bytes, lane_off);
-            else if (read_state)
-                halo[k] = ldrow(state_row + k * row_bytes, lane_off);
-        }
-    }
-    // Row loads: the R rows the next wave needs go out first, so they arrive first (vector loads
-    // return in order) and the hand-off below waits for them only.
     uint4 raw[BT];
-    int64_t slot[BT];
-    if (n == BT) {
+    int64_t lane_slot = -1;
+    if (has_rows) {
+        load_params<E, W>(pick(a.taps, tensor), pick(a.gamma, tensor), a.heads, D, h, d0, p);
+        // The first wave's R window rows before its span: the previous tile's last rows, the
+        // stored state, or zeros (loaded from a valid stand-in, the taps, and cleared later).
+        // The other waves get theirs from the wave before through LDS.
+        if (w == 0) {
+            const char* state_row = state + (int64_t)(slot_ok ? idx : 0) * R * row_bytes;
+            const char* hsrc = j > 0 ? x + (t0 - R) * stride_bytes
+                               : read_state ? state_row
+                                            : reinterpret_cast<const char*>(pick(a.taps, tensor));
+            const int64_t hstride = j > 0 ? stride_bytes : row_bytes;
 #pragma unroll
-        for (int i = BT - R; i < BT; ++i) raw[i] = ldrow(xb + i * stride_bytes, lane_off);
-#pragma unroll
-        for (int i = 0; i < BT - R; ++i) raw[i] = ldrow(xb + i * stride_bytes, lane_off);
-#pragma unroll
-        for (int i = 0; i < BT; ++i) slot[i] = a.slot[t0 + i];
-    } else {
-#pragma unroll
-        for (int i = 0; i < BT; ++i) {
-            raw[i] = i < n ? ldrow(xb + i * stride_bytes, lane_off) : make_uint4(0, 0, 0, 0);
-            slot[i] = i < n ? a.slot[t0 + i] : -1;
+            for (int k = 0; k < R; ++k) halo[k] = ldrow(hsrc + k * hstride, lane_off);
         }
+        // Past a short span's end the last row is read again (and not used). Lane l < BT loads
+        // token l's cache slot (one vector load instead of BT scalar ones, which the compiler
+        // would issue only after the rows arrive).
+        const int last = n - 1;
+#pragma unroll
+        for (int i = BT - R; i < BT; ++i)
+            raw[i] = ldrow(xb + (i < last ? i : last) * stride_bytes, lane_off);
+#pragma unroll
+        for (int i = 0; i < BT - R; ++i)
+            raw[i] = ldrow(xb + (i < last ? i : last) * stride_bytes, lane_off);
+        lane_slot = a.slot[t0 + (wl < last ? wl : last)];
     }
+    // LDS-staged halo: wave w hands its last R rows to wave w + 1, so a row is fetched once.
+    // (A wave with a short span is the last with rows in its tile; what it hands on is unused.)
     if (R > 0) {
-        if (w + 1 < NW && n == BT) {
+        if (has_rows && w + 1 < NW) {
 #pragma unroll
             for (int k = 0; k < R; ++k) handoff[w][k][wl] = raw[BT - R + k];
         }
         __syncthreads();
-        if (w > 0) {
+        if (has_rows && w > 0) {
 #pragma unroll
             for (int k = 0; k < R; ++k) halo[k] = handoff[w - 1][k][wl];
         }
     }
 
-    float win[W][VEC];
+    if (has_rows) {
+        if (first_span && !read_state) {
 #pragma unroll
-    for (int k = 0; k < R; ++k) E::widen(halo[k], win[k]);
-    const float inv_d = 1.0f / (float)D;
+            for (int k = 0; k < R; ++k) halo[k] = make_uint4(0, 0, 0, 0);
+        }
+        float win[W][VEC];
 #pragma unroll
-    for (int i = 0; i < BT; ++i) {
-        if (i < n) {
-            E::widen(raw[i], win[R]);
-            float o[VEC];
-            fused_row<E, W, LPH>(win, p, a.eps, inv_d, o);
-            sink.put(slot[i], active, o);
+        for (int k = 0; k < R; ++k) E::widen(halo[k], win[k]);
+        const float inv_d = 1.0f / (float)D;
+        // The window is a ring: token i's row goes to win[(i + R) % W], over the oldest row,
+        // which no later token reads, so advancing it costs no register moves.
+        // The first H1 tokens of the span are computed before any store is issued: with no store
+        // among them, the compiler knows which loads are still in flight and waits for each
+        // row just before its token, so those tokens are computed while later rows arrive. By
+        // then every row is in (one wait makes sure), their rows are stored, and the remaining
+        // tokens are computed and stored with nothing left in flight. (A conditional store
+        // between tokens would make the compiler wait, at every later token, for everything
+        // issued so far, that store included.) Holding H1 encoded rows costs registers; wide
+        // windows, with fewer waves per SIMD anyway, hold the whole span.
+        constexpr int H1 = W <= 4 ? BT / 2 : BT;
+        typename SinkFor<E, MX>::type::Enc out[H1];
 #pragma unroll
-            for (int k = 0; k < R; ++k)
+        for (int i = 0; i < H1; ++i) {
+            if (i < n) {
+                E::widen(raw[i], win[(i + R) % W]);
+                float o[VEC];
+                fused_row<E, W, LPH>(win, i % W, p, a.eps, inv_d, o);
+                out[i] = sink.encode(o);
+            }
+            // Token by token: left free, the scheduler widens later rows early and runs out of
+            // registers.
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_vmem();
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) win[k][v] = win[k + 1][v];
+        for (int i = 0; i < H1; ++i)
+            if (i < n) sink.write(lane_value(lane_slot, i), active, out[i]);
+#pragma unroll
+        for (int i = H1; i < BT; ++i) {
+            if (i < n) {
+                E::widen(raw[i], win[(i + R) % W]);
+                float o[VEC];
+                fused_row<E, W, LPH>(win, i % W, p, a.eps, inv_d, o);
+                sink.put(lane_value(lane_slot, i), active, o);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -502,27 +613,34 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(StepArgs a) {
     const int d0 = (c - h * LPH) * VEC;
     const int64_t row_bytes = (int64_t)a.heads * D * E::BYTES;
     const uint32_t lane_off = (uint32_t)(((int64_t)h * D + d0) * E::BYTES);
-    char* state = static_cast<char*>(a.state[tensor]);
+    char* state = static_cast<char*>(pick(a.state, tensor));
 
     const int32_t idx = uniform(a.state_idx ? a.state_idx[b] : (int32_t)b);
     const bool slot_ok = R > 0 && state != nullptr && idx >= 0 && idx < a.num_state_slots;
     char* srow = state + (int64_t)idx * R * row_bytes;  // used only when slot_ok
 
+    // Unconditional loads (a load under a branch makes the compiler wait for everything in flight
+    // at the merge): a sequence without a state slot reads the taps as a stand-in for its state
+    // rows (at least R rows long) and clears them afterwards.
+    const char* src = slot_ok ? srow : reinterpret_cast<const char*>(pick(a.taps, tensor));
+    const char* x = static_cast<const char*>(pick(a.x, tensor));
     uint4 raw[W];
 #pragma unroll
-    for (int k = 0; k < R; ++k)
-        raw[k] = slot_ok ? ldrow(srow + k * row_bytes, lane_off) : make_uint4(0, 0, 0, 0);
-    raw[R] = ldrow(static_cast<const char*>(a.x[tensor]) + b * a.x_stride[tensor] * E::BYTES,
-                   lane_off);
+    for (int k = 0; k < R; ++k) raw[k] = ldrow(src + k * row_bytes, lane_off);
+    raw[R] = ldrow(x + b * pick(a.x_stride, tensor) * E::BYTES, lane_off);
     const int64_t slot = a.slot[b];
 
     LaneParams<E, W> p;
-    load_params<E, W>(a.taps[tensor], a.gamma[tensor], a.heads, D, h, d0, p);
+    load_params<E, W>(pick(a.taps, tensor), pick(a.gamma, tensor), a.heads, D, h, d0, p);
+    if (!slot_ok) {
+#pragma unroll
+        for (int k = 0; k < R; ++k) raw[k] = make_uint4(0, 0, 0, 0);
+    }
     float win[W][VEC];
 #pragma unroll
     for (int k = 0; k < W; ++k) E::widen(raw[k], win[k]);
     float o[VEC];
-    fused_row<E, W, LPH>(win, p, a.eps, 1.0f / (float)D, o);
+    fused_row<E, W, LPH>(win, 0, p, a.eps, 1.0f / (float)D, o);
     const typename SinkFor<E, MX>::type sink(a, tensor, h, d0, D);
     sink.put(slot, true, o);
     if (slot_ok) {
@@ -553,11 +671,11 @@ __global__ void __launch_bounds__(kBlock) verify_kernel(StepArgs a, VerifyArgs v
     const int d0 = (c - h * LPH) * VEC;
     const int64_t row_bytes = (int64_t)a.heads * D * E::BYTES;
     const uint32_t lane_off = (uint32_t)(((int64_t)h * D + d0) * E::BYTES);
-    const char* x = static_cast<const char*>(a.x[tensor]);
-    const int64_t stride_bytes = a.x_stride[tensor] * E::BYTES;
+    const char* x = static_cast<const char*>(pick(a.x, tensor));
+    const int64_t stride_bytes = pick(a.x_stride, tensor) * E::BYTES;
     const PlainSink<E> sink(a, tensor, h, d0, D);
-    const char* state = static_cast<const char*>(a.state[tensor]);
-    char* snap = static_cast<char*>(va.snap[tensor]);
+    const char* state = static_cast<const char*>(pick(a.state, tensor));
+    char* snap = static_cast<char*>(pick(va.snap, tensor));
 
     const int64_t T = a.tokens;
     const int64_t start = uniform((int64_t)clamp_tok(a.cu[s], T));
@@ -568,7 +686,7 @@ __global__ void __launch_bounds__(kBlock) verify_kernel(StepArgs a, VerifyArgs v
     const bool slot_ok = R > 0 && state != nullptr && idx >= 0 && idx < a.num_state_slots;
 
     LaneParams<E, W> p;
-    load_params<E, W>(a.taps[tensor], a.gamma[tensor], a.heads, D, h, d0, p);
+    load_params<E, W>(pick(a.taps, tensor), pick(a.gamma, tensor), a.heads, D, h, d0, p);
     // Rolling window of raw rows (for bit-exact snapshots) and its widened copy.
     uint4 rw[R > 0 ? R : 1];
     float win[W][VEC];
@@ -596,7 +714,7 @@ __global__ void __launch_bounds__(kBlock) verify_kernel(StepArgs a, VerifyArgs v
             if (c0 + i < L) {
                 E::widen(raw[i], win[R]);
                 float o[VEC];
-                fused_row<E, W, LPH>(win, p, a.eps, inv_d, o);
+                fused_row<E, W, LPH>(win, 0, p, a.eps, inv_d, o);
                 sink.put(slot[i], true, o);
 #pragma unroll
                 for (int k = 0; k < R; ++k)
@@ -633,8 +751,8 @@ __global__ void __launch_bounds__(kBlock) commit_kernel(StepArgs a, VerifyArgs v
     const int d0 = (c - h * LPH) * VEC;
     const int64_t row_bytes = (int64_t)a.heads * D * E::BYTES;
     const uint32_t lane_off = (uint32_t)(((int64_t)h * D + d0) * E::BYTES);
-    char* state = static_cast<char*>(a.state[tensor]);
-    const char* snap = static_cast<const char*>(va.snap[tensor]);
+    char* state = static_cast<char*>(pick(a.state, tensor));
+    const char* snap = static_cast<const char*>(pick(va.snap, tensor));
 
     const int64_t T = a.tokens;
     const int64_t start = (int64_t)clamp_tok(a.cu[s], T);
@@ -680,13 +798,10 @@ __global__ void __launch_bounds__(kBlock) mx_quantize_kernel(StepArgs a) {
 // ------------------------------------------------------------------------------------------------
 using KernelFn = void (*)(StepArgs);
 
-template <int W>
-constexpr int tile_tokens() { return W <= 4 ? SC_PREFILL_TILE : SC_PREFILL_TILE_WIDE; }
-
 template <class E, int D, int W>
-constexpr KernelFn prefill_fn() { return prefill_kernel<E, D, W, tile_tokens<W>(), false>; }
+constexpr KernelFn prefill_fn() { return prefill_kernel<E, D, W, span_tokens<W, false>(), false>; }
 template <class E, int D, int W>
-constexpr KernelFn prefill_mx_fn() { return prefill_kernel<E, D, W, tile_tokens<W>(), true>; }
+constexpr KernelFn prefill_mx_fn() { return prefill_kernel<E, D, W, span_tokens<W, true>(), true>; }
 template <class E, int D, int W>
 constexpr KernelFn decode_fn() { return decode_kernel<E, D, W, false>; }
 template <class E, int D, int W>
@@ -721,13 +836,15 @@ int d_index(int D) { return D == 64 ? 0 : (D == 128 ? 1 : 2); }
 
 }  // namespace
 
-int prefill_tile_tokens(int, int, int width) {
-    return (kBlock / 64) * (width <= 4 ? tile_tokens<1>() : tile_tokens<8>());
+int prefill_tile_tokens(int, int, int width, bool mx) {
+    const int bt = width <= 4 ? (mx ? span_tokens<1, true>() : span_tokens<1, false>())
+                              : (mx ? span_tokens<8, true>() : span_tokens<8, false>());
+    return (kBlock / 64) * bt;
 }
 
 hipError_t launch_prefill(StepArgs a, int dtype, int head_dim, int width, bool mx,
                           hipStream_t stream) {
-    // One workgroup per (tile of 4 * tile_tokens tokens, 64-lane (1 KiB) column slice of the
+    // One workgroup per (tile of 4 spans of tokens, 64-lane (1 KiB) column slice of the
     // K|V rows); a.lane_blocks carries the number of slices.
     a.lane_blocks = (int32_t)((2 * (int64_t)a.lanes_per_tensor + 63) / 64);
     const int64_t blocks = (int64_t)a.tiles * a.lane_blocks;

@@ -48,7 +48,7 @@ hipError_t launch_verify(StepArgs a, VerifyArgs va, int dtype, int head_dim, int
 hipError_t launch_commit(StepArgs a, VerifyArgs va, int dtype, int head_dim, int width,
                          hipStream_t stream);
 
-// Tokens per prefill workgroup tile for a (dtype, head_dim, width) combination.
-int prefill_tile_tokens(int dtype, int head_dim, int width);
+// Tokens per prefill workgroup tile for a (dtype, head_dim, width, cache format) combination.
+int prefill_tile_tokens(int dtype, int head_dim, int width, bool mx);
 
 }  // namespace sc
