@@ -517,26 +517,31 @@ def pin_mxfp8_blocks():
     """Shared scale = 2^(floor(log2 amax) - 8) per 32-element block; an all-zero block gets the
     smallest scale; dequantized values sit within half a code step (relative 2^-4) of the input
     unless the element saturates at 448 * X."""
-    y = np.zeros((3, 64))
+    y = np.zeros((4, 64))
     y[0, :32] = np.linspace(-1.0, 1.0, 32)               # amax = 1 -> exponent -8
     y[0, 32:] = 3.0 * 2.0 ** -20                          # amax in [2^-19, 2^-18) -> -27
     y[1, :32] = 0.0
     y[1, 32:] = 1.99                                      # scaled 509.4 -> saturates to 448
     y[2] = np.random.default_rng(5).standard_normal(64) * 40.0
+    y[3, :32] = 2.0 ** -130 * np.arange(1, 33) / 32.0     # amax 2^-130 -> -138, clamped to -127
+    y[3, 32:] = 2.0 ** 140                                # -> 132, clamped to 127 (scaled 2^13)
     codes, scales = oracle.mxfp8_quantize(y)
     assert scales[0, 0] == 127 - 8 and scales[0, 1] == 127 - 27
     assert scales[1, 0] == 0 and (codes[1, :32] == 0).all()
     assert (codes[1, 32:] == 0x7E).all() and scales[1, 1] == 127 - 8
     assert codes[0, 31] == 0x78 and codes[0, 0] == 0xF8  # +-1.0 -> +-256 = 2^8 -> exponent field 15
+    assert scales[3, 0] == 0 and scales[3, 1] == 254 and (codes[3, 32:] == 0x7E).all()
+    # 2^-130 * k/32 * 2^127 = k * 2^-8: subnormal codes 2k (k <= 3), then normals
+    assert codes[3, 0] == 2 and codes[3, 2] == 6 and codes[3, 3] == 0x08
     deq = oracle.mxfp8_dequantize(codes, scales)
-    blocks = y.reshape(3, 2, 32)
+    blocks = y.reshape(4, 2, 32)
     x = np.ldexp(1.0, scales.astype(np.int64) - 127)[..., None]
-    sat = (np.abs(blocks) > 448.0 * x).reshape(3, 64)
-    sub = (np.abs(blocks) < 2.0 ** -6 * x).reshape(3, 64)
+    sat = (np.abs(blocks) > 448.0 * x).reshape(4, 64)
+    sub = (np.abs(blocks) < 2.0 ** -6 * x).reshape(4, 64)
     err = np.abs(deq - y)
     ok = ~sat & ~sub
     assert (err[ok] <= 2.0 ** -4 * np.abs(y[ok]) * (1 + 1e-12)).all()
-    assert np.allclose(deq[sat], np.sign(y[sat]) * 448.0 * np.repeat(x.reshape(3, 2), 32, 1)[sat])
+    assert np.allclose(deq[sat], np.sign(y[sat]) * 448.0 * np.repeat(x.reshape(4, 2), 32, 1)[sat])
 
 
 ALL_PINS = [
