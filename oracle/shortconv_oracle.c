@@ -233,3 +233,133 @@ int sc_oracle_decode(int dtype, int64_t H, int64_t D, int64_t W, int64_t B, cons
     }
     return 0;
 }
+
+/*
+ * Backward of the prefill step, one tensor: the gradients of a loss through the definition at the
+ * top of this file, for training (the news item's paragraph 3: the RL trainer runs the same model
+ * with train/infer-consistent kernels). Nothing on the pages states it; it is the chain rule
+ * applied to that definition, step by step:
+ *   chat[p,h,d]  = c[p,h,d] / r[p,h]
+ *   dchat        = g[p,h,d] * gamma[d]                            (g = dLoss/dy)
+ *   dgamma[d]   += g[p,h,d] * chat[p,h,d]                         (over every token and head)
+ *   dc[p,h,d]    = (dchat - chat * (1/D) sum_j dchat[j] chat[j]) / r[p,h]
+ *   dtaps[k,h,d] += dc[p,h,d] * e[p+k,h,d]                        (over every sequence and token)
+ *   de[i,h,d]    = sum_{k : 0 <= i-k < L} taps[k,h,d] * dc[i-k,h,d]
+ *                  + gs[i-L,h,d] when L <= i < L+W-1               (gs = dLoss/d(new state))
+ *   dx[cu[s]+t]  = de[t+W-1]
+ *   dstate[s,i]  = de[i] for i < W-1 when the window came from the stored state, else 0
+ *
+ *  x, cu, taps, gamma, eps, state, n_state, state_idx, has_init   as for sc_oracle_prefill
+ *  g          fp64 [T][H][D]
+ *  gs         fp64 [n_seq][W-1][H][D] or NULL (no loss on the new state)
+ *  dx         out fp64 [T][H][D]
+ *  dtaps      out fp64 [W][H][D];   dgamma out fp64 [D]
+ *  dstate     out fp64 [n_seq][W-1][H][D] or NULL
+ *
+ * The sums over sequences (dtaps) and over sequences and heads (dgamma) are taken per
+ * (sequence, head) unit first and then added in unit order, so the result does not depend on the
+ * thread count. Returns 0, or -1 on bad sizes.
+ */
+int sc_oracle_backward(int dtype, int64_t H, int64_t D, int64_t W, int64_t n_seq,
+                       const int64_t* cu, const void* x, int64_t x_stride, const float* taps,
+                       const float* gamma, float eps, const void* state, int64_t n_state,
+                       const int64_t* state_idx, const uint8_t* has_init, const double* g,
+                       const double* gs, double* dx, double* dtaps, double* dgamma,
+                       double* dstate, int nthreads)
+{
+    if (H <= 0 || D <= 0 || W <= 0 || n_seq < 0 || x_stride < H * D) return -1;
+    if (dtype != ORC_F32 && dtype != ORC_BF16) return -1;
+    const int64_t R = W - 1;
+    const int64_t units = n_seq * H;
+    double* part_taps = (double*)calloc((size_t)(units > 0 ? units : 1) * W * D, sizeof(double));
+    double* part_gamma = (double*)calloc((size_t)(units > 0 ? units : 1) * D, sizeof(double));
+    (void)nthreads;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t u = 0; u < units; ++u) {
+        const int64_t s = u / H, h = u % H;
+        const int64_t start = cu[s], L = cu[s + 1] - cu[s];
+        const int64_t idx = state_idx[s];
+        const int from_state = state != NULL && idx >= 0 && idx < n_state && has_init[s];
+        const int64_t E = R + L; /* rows of e */
+        double* e = (double*)malloc((size_t)(E > 0 ? E : 1) * D * sizeof(double));
+        double* dc = (double*)malloc((size_t)(L > 0 ? L : 1) * D * sizeof(double));
+        double* c = (double*)malloc((size_t)D * sizeof(double));
+        double* pt = part_taps + u * W * D;
+        double* pg = part_gamma + u * D;
+
+        /* the window rows e[0 .. R+L) of this sequence and head */
+        for (int64_t i = 0; i < E; ++i)
+            for (int64_t d = 0; d < D; ++d)
+                e[i * D + d] = i < R ? (from_state ? widen(state, ((idx * R + i) * H + h) * D + d,
+                                                           dtype)
+                                                   : 0.0)
+                                     : widen(x, (start + i - R) * x_stride + h * D + d, dtype);
+
+        for (int64_t p = 0; p < L; ++p) {
+            /* forward quantities of token p */
+            double sumsq = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < W; ++k)
+                    acc += (double)taps[(k * H + h) * D + d] * e[(p + k) * D + d];
+                c[d] = acc;
+                sumsq += acc * acc;
+            }
+            const double rp = sqrt(sumsq / (double)D + (double)eps);
+            /* through the norm and gamma */
+            double proj = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                const double gd = g[((start + p) * H + h) * D + d];
+                const double chat = c[d] / rp;
+                pg[d] += gd * chat;
+                proj += gd * (double)gamma[d] * chat;
+            }
+            proj /= (double)D;
+            for (int64_t d = 0; d < D; ++d) {
+                const double gd = g[((start + p) * H + h) * D + d];
+                const double chat = c[d] / rp;
+                dc[p * D + d] = (gd * (double)gamma[d] - chat * proj) / rp;
+            }
+            /* through the convolution: the taps */
+            for (int64_t k = 0; k < W; ++k)
+                for (int64_t d = 0; d < D; ++d)
+                    pt[k * D + d] += dc[p * D + d] * e[(p + k) * D + d];
+        }
+
+        /* through the convolution: its input rows, plus the loss on the new state */
+        for (int64_t i = 0; i < E; ++i) {
+            for (int64_t d = 0; d < D; ++d) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < W; ++k) {
+                    const int64_t p = i - k;
+                    if (p >= 0 && p < L) acc += (double)taps[(k * H + h) * D + d] * dc[p * D + d];
+                }
+                if (gs && i >= L) acc += gs[((s * R + (i - L)) * H + h) * D + d];
+                if (i >= R)
+                    dx[((start + i - R) * H + h) * D + d] = acc;
+                else if (dstate)
+                    dstate[((s * R + i) * H + h) * D + d] = from_state ? acc : 0.0;
+            }
+        }
+        free(e);
+        free(dc);
+        free(c);
+    }
+
+    for (int64_t k = 0; k < W; ++k)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t d = 0; d < D; ++d) {
+                double acc = 0.0;
+                for (int64_t s = 0; s < n_seq; ++s) acc += part_taps[((s * H + h) * W + k) * D + d];
+                dtaps[(k * H + h) * D + d] = acc;
+            }
+    for (int64_t d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int64_t u = 0; u < units; ++u) acc += part_gamma[u * D + d];
+        dgamma[d] = acc;
+    }
+    free(part_taps);
+    free(part_gamma);
+    return 0;
+}

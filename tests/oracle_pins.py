@@ -544,6 +544,149 @@ def pin_mxfp8_blocks():
     assert np.allclose(deq[sat], np.sign(y[sat]) * 448.0 * np.repeat(x.reshape(4, 2), 32, 1)[sat])
 
 
+# ------------------------------------------------------------------------------------------------
+# Backward (the gradients of the step, for training)
+# ------------------------------------------------------------------------------------------------
+def _bwd_case(dtype="f32", W=4, H=2, D=8, lens=(6, 2, 0, 9), hin=(1, 0, 1, 1), seed=11, eps=None):
+    spec = workloads.Spec(dtype=dtype, H=H, D=D, W=W, seed=seed, prefill_lens=list(lens),
+                          has_init=list(hin))
+    if eps is not None:
+        spec.eps = eps
+    w = workloads.build(spec)
+    st = w.steps[0]
+    g = np.random.default_rng(seed).standard_normal((st.tokens, H, D))
+    gs = (np.random.default_rng(seed + 1).standard_normal((st.num_seqs, W - 1, H, D))
+          if W > 1 else None)
+    return w, st, g, gs
+
+
+def _loss(w, st, g, gs, x=None, taps=None, gamma=None, state=None):
+    """sum(g * y) + sum(gs * new state), through the forward oracle."""
+    y, ns, _ = oracle.prefill_one(st.k if x is None else x, st.cu_seqlens,
+                                  w.k_taps if taps is None else taps,
+                                  w.k_gamma if gamma is None else gamma, w.eps,
+                                  w.k_state if state is None else state, st.state_idx,
+                                  st.has_init)
+    total = float((g * y).sum())
+    if gs is not None:
+        total += float((gs * oracle.widen(ns)).sum())
+    return total
+
+
+def _central_differences(f, arr, h=2.0 ** -12):
+    """d f / d arr by central differences; arr is fp32, and arr +- h is exact in fp32 for every
+    |value| < 2^11, so the only errors are the O(h^2) truncation and fp64 roundoff."""
+    out = np.zeros(arr.shape, np.float64)
+    flat = arr.reshape(-1)
+    for i in range(flat.size):
+        keep = flat[i]
+        flat[i] = keep + np.float32(h)
+        up = f()
+        flat[i] = keep - np.float32(h)
+        down = f()
+        flat[i] = keep
+        out.reshape(-1)[i] = (up - down) / (2.0 * h)
+    return out
+
+
+def pin_backward_finite_differences():
+    """Every gradient of the backward oracle equals the central difference of the forward
+    oracle's loss sum(g*y) + sum(gs*new_state): input rows, taps, gamma and the state pool
+    (through has_init, an empty sequence and one shorter than the window)."""
+    for W in (4, 2):
+        w, st, g, gs = _bwd_case(W=W)
+        gr = oracle.backward_one(st.k, st.cu_seqlens, w.k_taps, w.k_gamma, w.eps, w.k_state,
+                                 st.state_idx, st.has_init, g, gs)
+        x = st.k.copy()
+        taps = w.k_taps.copy()
+        gamma = w.k_gamma.copy()
+        pool = w.k_state.copy()
+        fd_x = _central_differences(lambda: _loss(w, st, g, gs, x=x), x)
+        fd_t = _central_differences(lambda: _loss(w, st, g, gs, taps=taps), taps)
+        fd_g = _central_differences(lambda: _loss(w, st, g, gs, gamma=gamma), gamma)
+        fd_s = _central_differences(lambda: _loss(w, st, g, gs, state=pool), pool)
+        an_s = np.zeros_like(fd_s)
+        for s in range(st.num_seqs):
+            an_s[st.state_idx[s]] += gr.dstate[s]
+        for name, fd, an in (("dx", fd_x, gr.dx), ("dtaps", fd_t, gr.dtaps),
+                             ("dgamma", fd_g, gr.dgamma), ("dstate", fd_s, an_s)):
+            assert np.allclose(an, fd, rtol=1e-6, atol=1e-6), f"{name} != finite differences (W={W})"
+    # bf16 storage changes nothing but the widening: same values stored as fp32 give the same
+    # gradients, bit for bit
+    w, st, g, gs = _bwd_case(dtype="bf16")
+    a = oracle.backward_one(st.k, st.cu_seqlens, w.k_taps, w.k_gamma, w.eps, w.k_state,
+                            st.state_idx, st.has_init, g, gs)
+    b = oracle.backward_one(workloads.bf16_bits_to_f32(st.k), st.cu_seqlens, w.k_taps, w.k_gamma,
+                            w.eps, workloads.bf16_bits_to_f32(w.k_state), st.state_idx,
+                            st.has_init, g, gs)
+    for f in ("dx", "dtaps", "dgamma", "dstate"):
+        assert np.array_equal(getattr(a, f), getattr(b, f)), f"bf16 {f}"
+
+
+def pin_backward_torch_autograd():
+    """The backward oracle == PyTorch fp64 autograd through conv1d(groups=channels) and rms_norm,
+    with the initial state prepended and a loss on the new state."""
+    for W, dtype in ((4, "bf16"), (3, "f32")):
+        w, st, g, gs = _bwd_case(dtype=dtype, W=W, H=3, D=64, lens=(20, 1, 0, 37), hin=(1, 1, 0, 1),
+                                 seed=21)
+        gr = oracle.backward_one(st.k, st.cu_seqlens, w.k_taps, w.k_gamma, w.eps, w.k_state,
+                                 st.state_idx, st.has_init, g, gs)
+        H, D, R, C = 3, 64, W - 1, 3 * 64
+        x = torch.from_numpy(oracle.widen(st.k)).requires_grad_()
+        taps = torch.from_numpy(w.k_taps.astype(np.float64)).requires_grad_()
+        gamma = torch.from_numpy(w.k_gamma.astype(np.float64)).requires_grad_()
+        z = torch.from_numpy(oracle.widen(w.k_state)[st.state_idx]).requires_grad_()
+        weight = taps.reshape(W, C).T.unsqueeze(1)
+        loss = torch.zeros((), dtype=torch.float64)
+        cu = st.cu_seqlens
+        for s in range(st.num_seqs):
+            a, b = int(cu[s]), int(cu[s + 1])
+            zs = z[s] if st.has_init[s] else torch.zeros((R, H, D), dtype=torch.float64)
+            e = torch.cat([zs, x[a:b]], 0)
+            if b > a:
+                c = F.conv1d(e.reshape(R + b - a, C).T[None], weight, groups=C)[0].T
+                y = F.rms_norm(c.reshape(b - a, H, D), (D,), weight=gamma, eps=EPS32)
+                loss = loss + (torch.from_numpy(g[a:b]) * y).sum()
+            loss = loss + (torch.from_numpy(gs[s]) * e[b - a:b - a + R]).sum()
+        loss.backward()
+        for name, ours, ref in (("dx", gr.dx, x.grad), ("dtaps", gr.dtaps, taps.grad),
+                                ("dgamma", gr.dgamma, gamma.grad), ("dstate", gr.dstate, z.grad)):
+            ref = ref.numpy()
+            assert np.allclose(ours, ref, rtol=1e-10, atol=1e-10 * np.abs(ref).max()), \
+                f"{name} != torch autograd (W={W}, {dtype})"
+
+
+def pin_backward_invariants():
+    """Euler's theorem on the loss sum(g*y) + sum(gs*new_state), exact in exact arithmetic:
+    with eps = 0, y is invariant to scaling one head's taps, so sum_k,d dtaps*taps = 0 per head;
+    y is invariant and the new state homogeneous of degree 1 in (x, initial window), so
+    sum dx*x + sum dstate*z = sum gs*new_state; and y is linear in gamma, so
+    sum dgamma*gamma = sum g*y (any eps)."""
+    for W in (4, 8, 1):
+        w, st, g, gs = _bwd_case(W=W, D=64, lens=(12, 2, 30), hin=(1, 1, 0), eps=0.0, seed=31)
+        gr = oracle.backward_one(st.k, st.cu_seqlens, w.k_taps, w.k_gamma, w.eps, w.k_state,
+                                 st.state_idx, st.has_init, g, gs)
+        t64 = w.k_taps.astype(np.float64)
+        per_head = (gr.dtaps * t64).sum(axis=(0, 2))
+        scale = np.abs(gr.dtaps * t64).sum(axis=(0, 2))
+        assert (np.abs(per_head) <= 1e-12 * scale).all(), f"taps scale invariance (W={W})"
+        y, ns, _ = oracle.prefill_one(st.k, st.cu_seqlens, w.k_taps, w.k_gamma, w.eps, w.k_state,
+                                      st.state_idx, st.has_init)
+        x64 = oracle.widen(st.k)
+        lhs_terms = [gr.dx * x64]
+        rhs = 0.0
+        if W > 1:
+            z = oracle.widen(w.k_state)[st.state_idx] * st.has_init[:, None, None, None]
+            lhs_terms.append(gr.dstate * z)
+            rhs = float((gs * oracle.widen(ns)).sum())
+        lhs = sum(float(t.sum()) for t in lhs_terms)
+        mag = sum(float(np.abs(t).sum()) for t in lhs_terms) + abs(rhs)
+        assert abs(lhs - rhs) <= 1e-12 * mag, f"input homogeneity (W={W})"
+        gy = float((g * y).sum())
+        dg = float((gr.dgamma * w.k_gamma.astype(np.float64)).sum())
+        assert abs(dg - gy) <= 1e-12 * float(np.abs(g * y).sum()), f"gamma linearity (W={W})"
+
+
 ALL_PINS = [
     pin_exact_rational,
     pin_torch_conv1d_rmsnorm,
@@ -562,4 +705,7 @@ ALL_PINS = [
     pin_verify_snapshots_and_commit,
     pin_mxfp8_codes,
     pin_mxfp8_blocks,
+    pin_backward_finite_differences,
+    pin_backward_torch_autograd,
+    pin_backward_invariants,
 ]

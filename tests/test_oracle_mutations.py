@@ -34,6 +34,24 @@ MUTATIONS = [
     ("decode_state_not_shifted", "((idx * R + j + 1) * H + h)", "((idx * R + j) * H + h)", 0),
     ("decode_eps_dropped", "sqrt(ss / (double)D + (double)eps)", "sqrt(ss / (double)D)", -1),
     ("cond_missing_gamma", "cond[o] = fabs((double)gamma[d]) * a[d] / r;", "cond[o] = a[d] / r;", 0),
+    # the backward
+    ("bwd_projection_dropped", "chat * proj) / rp;", "0.0 * proj) / rp;", 0),
+    ("bwd_sum_instead_of_mean", "proj /= (double)D;", "", 0),
+    ("bwd_not_divided_by_r", "chat * proj) / rp;", "chat * proj);", 0),
+    ("bwd_projection_without_gamma", "proj += gd * (double)gamma[d] * chat;", "proj += gd * chat;", 0),
+    ("bwd_dgamma_with_gamma", "pg[d] += gd * chat;", "pg[d] += gd * chat * (double)gamma[d];", 0),
+    ("bwd_input_taps_flipped",
+     "if (p >= 0 && p < L) acc += (double)taps[(k * H + h) * D + d] * dc[p * D + d];",
+     "if (p >= 0 && p < L) acc += (double)taps[((W - 1 - k) * H + h) * D + d] * dc[p * D + d];", 0),
+    ("bwd_dtaps_rows_flipped", "pt[k * D + d] += dc[p * D + d] * e[(p + k) * D + d];",
+     "pt[k * D + d] += dc[p * D + d] * e[(p + W - 1 - k) * D + d];", 0),
+    ("bwd_new_state_loss_shifted", "if (gs && i >= L)", "if (gs && i > L)", 0),
+    ("bwd_dstate_ignores_has_init", "= from_state ? acc : 0.0;", "= acc;", 0),
+    ("bwd_dx_shifted", "dx[((start + i - R) * H + h) * D + d] = acc;",
+     "dx[((start + (i > R ? i - R - 1 : i - R)) * H + h) * D + d] = acc;", 0),
+    ("bwd_dtaps_one_sequence", "acc += part_taps[((s * H + h) * W + k) * D + d];",
+     "acc = part_taps[((s * H + h) * W + k) * D + d];", 0),
+    ("bwd_eps_dropped", "sqrt(sumsq / (double)D + (double)eps)", "sqrt(sumsq / (double)D)", 0),
 ]
 
 
