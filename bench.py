@@ -37,17 +37,23 @@ sys.path.insert(0, ROOT)
 METRIC = "fused ShortConv K/V tokens/s + achieved HBM GB/s (% of 8 TB/s), prefill & decode"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
 MALL_BYTES = 256 << 20          # MI355X Infinity Cache
-KERNEL_SRC = os.path.join(ROOT, "causal_short_convolution_amd", "csrc", "kernels.hip")
+KERNEL_SRC = [os.path.join(ROOT, "causal_short_convolution_amd", "csrc", f)
+              for f in ("kernels.hip", "device_common.h")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_varlen_bf16_traffic.md")
 WORKLOADS = {"tiny_ref": 1, "varlen_prefill": 2, "decode": 3, "long_prefill": 4, "mixed": 5}
 COPY_BYTES = 512 << 20          # calibration copy: 512 MiB read + 512 MiB written
 KERNELS = ("prefill_kernel", "decode_kernel", "verify_kernel", "commit_kernel",
-           "mx_quantize_kernel")
+           "mx_quantize_kernel", "backward_kernel", "backward_chunk_kernel", "backward_taps_kernel",
+           "backward_gamma_kernel")
 
 
 def kernel_source_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 of the prefill kernel's sources (kernels.hip, then device_common.h)."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 # ------------------------------------------------------------------------------------------------
@@ -110,8 +116,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the MXFP8-cache and speculative-verify measurements")
-    ap.add_argument("--only", default=None, choices=["main", "decode", "mxfp8", "verify"],
+                    help="skip the MXFP8-cache, speculative-verify and backward measurements")
+    ap.add_argument("--only", default=None,
+                    choices=["main", "decode", "mxfp8", "verify", "backward"],
                     help="run one measurement only (for profiling); prints no JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -310,6 +317,59 @@ def measure_verify(torch, steps, warmup, seed, graph=True):
             "achieved_GBps": (vb + cb) / (per_ms * 1e-3) / 1e9}
 
 
+def backward_bytes(w):
+    """Algorithmic bytes of one backward call over workload w's prefill: per token read the K
+    and V rows and their output gradients and write the two input-gradient rows (6R); per
+    sequence that resumes from a stored state read its 2 (W-1) R state rows; taps and gamma read,
+    their gradients written. The fp32 partials the kernel passes through its workspace are not
+    counted (they are the implementation's, not the method's)."""
+    st = w.steps[0]
+    E = 4 if w.dtype == "f32" else 2
+    R = w.H * w.D * E
+    n_init = int(st.has_init.sum()) if w.W > 1 else 0
+    params = 2 * 2 * (w.W * w.H * w.D * 4 + w.D * 4)
+    return st.tokens * 6 * R + n_init * 2 * (w.W - 1) * R + st.num_seqs * 9 + 4 + params
+
+
+def measure_backward(torch, w, steps, warmup, graph=True):
+    """One backward call (shortconv_kv_backward) over the prefill of workload w, with random
+    output gradients; no new-state loss, no initial-state gradient (a fresh training batch)."""
+    import numpy as np
+    import causal_short_convolution_amd as sc
+    st = w.steps[0]
+    dev = "cuda:0"
+    alg = backward_bytes(w)
+    n_rep = max(2, math.ceil(2 * MALL_BYTES / alg) + 1)
+    reps = device_replicas(w, torch, n_rep)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    T, H, D, W = st.tokens, w.H, w.D, w.W
+    ws = torch.empty(max(16, sc.shortconv_kv_backward_workspace_size(T, st.num_seqs, H, D, W, dt)),
+                     dtype=torch.uint8, device=dev)
+    grads = [torch.empty((W, H, D), device=dev) for _ in range(2)] + \
+            [torch.empty((D,), device=dev) for _ in range(2)]
+    hinit = torch.from_numpy(st.has_init.astype(np.uint8)).to(dev)
+    fns = []
+    for r in reps:
+        d = r["steps"][0]
+        dyk = torch.randn((T, H, D), device=dev).to(dt)
+        dyv = torch.randn((T, H, D), device=dev).to(dt)
+        dk, dv = torch.empty_like(dyk), torch.empty_like(dyv)
+
+        def go(d=d, r=r, dyk=dyk, dyv=dyv, dk=dk, dv=dv):
+            sc.shortconv_kv_backward(d["k"], d["v"], d["cu"], d["k_taps"], d["v_taps"],
+                                     d["k_gamma"], d["v_gamma"], d["eps"], r["k_state"],
+                                     r["v_state"], d["sidx"], hinit, dyk, dyv, dk, dv, *grads,
+                                     workspace=ws)
+        fns.append(go)
+    wall, dev_ms = time_steps(torch, fns, steps, warmup, graph)
+    del reps, fns
+    per_ms = dev_ms / steps
+    return {"workload": w.name, "tokens_per_step": T, "launches_per_step": 2, "replicas": n_rep,
+            "ms_per_step": 1e3 * wall / steps, "tokens_per_s": T * steps / wall,
+            "kernel_us_mean": 1e3 * per_ms, "algorithmic_bytes": alg,
+            "workspace_bytes": ws.numel(), "achieved_GBps": alg / (per_ms * 1e-3) / 1e9}
+
+
 def copy_ceiling(torch, bytes_moved, steps, warmup):
     """Same-bytes ceiling: a plain non-temporal copy that reads bytes_moved/2 and writes
     bytes_moved/2, in the same rotating-replica regime and graph replay as the fused kernel."""
@@ -392,7 +452,7 @@ def summarize_profile(dirs):
 
     def short(name):
         return name.replace("sc::(anonymous namespace)::", "").replace(
-            "(anonymous namespace)::", "").replace("void ", "")
+            "(anonymous namespace)::", "").replace("void ", "").replace("sc::", "")
     out = []
     per = {}  # (kernel, counter) -> values per dispatch
     for d in dirs:
@@ -482,6 +542,8 @@ def main():
         elif args.only == "decode":
             m = measure(torch, workloads.config(3, seed=args.seed), args.steps, args.warmup,
                         lambda r: workloads.config(3, seed=args.seed + 1000 * r), graph)
+        elif args.only == "backward":
+            m = measure_backward(torch, w, args.steps, args.warmup, graph)
         else:
             m = measure_verify(torch, args.steps, args.warmup, args.seed, graph)
         print(f"bench.py: {args.only}: {m['kernel_us_mean']:.2f} us per step, "
@@ -505,6 +567,10 @@ def main():
         vm = measure_verify(torch, args.steps, args.warmup, args.seed, graph)
         extra["spec_verify"] = {**_round(vm),
                                 "frac_of_hbm_peak": vm["achieved_GBps"] / HBM_PEAK_GBPS}
+        if all(st.kind == "prefill" for st in w.steps):
+            bm = measure_backward(torch, w, args.steps, args.warmup, graph)
+            extra["backward"] = {**_round(bm),
+                                 "frac_of_hbm_peak": bm["achieved_GBps"] / HBM_PEAK_GBPS}
     if args.calibrate_copy:
         calibration_copy(torch)
     ceil = copy_ceiling(torch, main_m["algorithmic_bytes"], args.steps, args.warmup)

@@ -3,11 +3,13 @@
 Causal depthwise convolution over tokens of the projected K and V, per-head RMSNorm, paged
 KV-cache write and rolling conv-state update, in one HIP kernel per call; plus speculative
 verification with per-token conv-state snapshots and the commit of an accepted prefix, and
-variants that write MXFP8 (OCP microscaling) cache rows. The
+variants that write MXFP8 (OCP microscaling) cache rows, and the backward of the step for
+training. The
 compute lives in ``libshortconv.so`` (C ABI, ``include/shortconv.h``); this package only
 marshals torch tensors.
 """
 from ._binding import (LIBRARY_PATH, ShortConvError, abi_version, last_error, load_library,
+                       shortconv_kv_backward, shortconv_kv_backward_workspace_size,
                        shortconv_kv_decode, shortconv_kv_decode_mxfp8, shortconv_kv_prefill,
                        shortconv_kv_prefill_mxfp8, shortconv_kv_verify, shortconv_mxfp8_quantize,
                        shortconv_state_commit)
@@ -18,6 +20,8 @@ __all__ = [
     "abi_version",
     "last_error",
     "load_library",
+    "shortconv_kv_backward",
+    "shortconv_kv_backward_workspace_size",
     "shortconv_kv_decode",
     "shortconv_kv_decode_mxfp8",
     "shortconv_kv_prefill",

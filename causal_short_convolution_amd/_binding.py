@@ -61,6 +61,12 @@ def load_library(path: str = LIBRARY_PATH):
                                               P, P, P, P, I64, I32, I32, I32, I32, P]
     lib.shortconv_mxfp8_quantize.restype = ctypes.c_int
     lib.shortconv_mxfp8_quantize.argtypes = [P, I64, I64, I32, I32, I32, P, P, P]
+    lib.shortconv_kv_backward.restype = ctypes.c_int
+    lib.shortconv_kv_backward.argtypes = [P, P, I64, I64, P, I32, I64, P, P, P, P, F, P, P, I64,
+                                          P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                          ctypes.c_size_t, I32, I32, I32, I32, P]
+    lib.shortconv_kv_backward_workspace_size.restype = ctypes.c_size_t
+    lib.shortconv_kv_backward_workspace_size.argtypes = [I64, I32, I32, I32, I32, I32]
     lib.shortconv_last_error.restype = ctypes.c_char_p
     lib.shortconv_last_error.argtypes = []
     lib.shortconv_abi_version.restype = ctypes.c_int
@@ -226,4 +232,45 @@ def shortconv_mxfp8_quantize(x, codes, scales, *,
         rc = lib.shortconv_mxfp8_quantize(_ptr(x), _rows(x, "x"), rows, H, D, SC_DTYPE[x.dtype],
                                           _ptr(codes), _ptr(scales),
                                           _stream_handle(x.device, stream))
+    _check(rc)
+
+
+def shortconv_kv_backward_workspace_size(total_tokens, num_seqs, num_heads, head_dim, width,
+                                         dtype) -> int:
+    """Bytes of workspace ``shortconv_kv_backward`` needs (see include/shortconv.h)."""
+    lib = load_library()
+    code = SC_DTYPE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    n = lib.shortconv_kv_backward_workspace_size(int(total_tokens), int(num_seqs), int(num_heads),
+                                                 int(head_dim), int(width), code)
+    if n == ctypes.c_size_t(-1).value:
+        raise ShortConvError(-1, last_error())
+    return int(n)
+
+
+def shortconv_kv_backward(k, v, cu_seqlens, k_taps, v_taps, k_gamma, v_gamma, eps, k_state,
+                          v_state, state_idx, has_initial_state, dy_k, dy_v, dk, dv, dk_taps,
+                          dv_taps, dk_gamma, dv_gamma, *, dstate_out=(None, None),
+                          dstate_in=(None, None), workspace: Optional[torch.Tensor] = None,
+                          stream: Optional[torch.cuda.Stream] = None) -> None:
+    """Gradients of the prefill step (see include/shortconv.h): from dy_k/dy_v (and optionally the
+    new-state gradients ``dstate_out``) into dk/dv, the tap and gamma gradients and optionally the
+    initial-window gradients ``dstate_in``. ``workspace`` (uint8 device tensor) is allocated here
+    when not given."""
+    lib = load_library()
+    W, H, D = k_taps.shape
+    N = cu_seqlens.shape[0] - 1
+    T = k.shape[0]
+    S = k_state.shape[0] if k_state is not None else 0
+    need = shortconv_kv_backward_workspace_size(T, N, H, D, W, k.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=k.device)
+    with torch.cuda.device(k.device):
+        rc = lib.shortconv_kv_backward(
+            _ptr(k), _ptr(v), _rows(k, "k"), _rows(v, "v"), _ptr(cu_seqlens), N, T, _ptr(k_taps),
+            _ptr(v_taps), _ptr(k_gamma), _ptr(v_gamma), float(eps), _ptr(k_state), _ptr(v_state),
+            S, _ptr(state_idx), _ptr(has_initial_state), _ptr(dy_k), _ptr(dy_v),
+            _ptr(dstate_out[0]), _ptr(dstate_out[1]), _ptr(dk), _ptr(dv), _ptr(dk_taps),
+            _ptr(dv_taps), _ptr(dk_gamma), _ptr(dv_gamma), _ptr(dstate_in[0]), _ptr(dstate_in[1]),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), H, D, W,
+            SC_DTYPE[k.dtype], _stream_handle(k.device, stream))
     _check(rc)

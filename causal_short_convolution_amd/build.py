@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libshortconv.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("kernels.hip", "abi.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("kernels.hip", "backward.hip", "abi.hip")]
 # measurement companion used by bench.py (same-bytes copy ceiling); not part of the C ABI
 PROBE_LIB = os.path.join(HERE, "libscprobe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "copy_probe.hip")]

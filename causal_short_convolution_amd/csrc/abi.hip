@@ -1,6 +1,8 @@
 // C ABI of the fused ShortConv K/V step: host-side validation, problem geometry and launch.
 // The operation, layouts and error behaviour are specified in include/shortconv.h.
 #include <stdarg.h>
+#include <stddef.h>
+#include <stdint.h>
 #include <stdio.h>
 
 #include "shortconv.h"
@@ -350,6 +352,134 @@ SC_API int shortconv_state_commit(const void* k_snap, const void* v_snap, int32_
     va.accepted = accepted;
     va.max_tokens = max_tokens;
     hipError_t e = sc::launch_commit(a, va, dtype, head_dim, width, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(SC_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return SC_OK;
+}
+
+namespace {
+
+// Shape checks of the backward (the same limits as the forward). Returns SC_OK or an error.
+int check_backward_shape(const char* fn, int64_t total_tokens, int32_t num_seqs, int32_t heads,
+                         int32_t D, int32_t W, int32_t dtype) {
+    if (dtype != SC_DTYPE_F32 && dtype != SC_DTYPE_BF16)
+        return fail(SC_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+    if (D != 64 && D != 128 && D != 256)
+        return fail(SC_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128, 256}", fn, D);
+    if (W < 1 || W > 8) return fail(SC_ERR_UNSUPPORTED, "%s: width %d not in [1, 8]", fn, W);
+    if (heads < 1) return fail(SC_ERR_INVALID, "%s: num_heads %d < 1", fn, heads);
+    if ((int64_t)heads * D > (int64_t)1 << 20)
+        return fail(SC_ERR_UNSUPPORTED, "%s: num_heads too large", fn);
+    if (num_seqs < 0) return fail(SC_ERR_INVALID, "%s: num_seqs < 0", fn);
+    if (total_tokens < 0 || total_tokens > INT32_MAX)
+        return fail(SC_ERR_INVALID, "%s: total_tokens must be in [0, 2^31)", fn);
+    const sc::BwdShape sh = sc::backward_shape(total_tokens, num_seqs, heads, D, W, dtype);
+    if (sh.groups * sh.slices > INT32_MAX || sh.tiles > INT32_MAX)
+        return fail(SC_ERR_UNSUPPORTED, "%s: problem too large for one launch", fn);
+    return SC_OK;
+}
+
+}  // namespace
+
+SC_API size_t shortconv_kv_backward_workspace_size(int64_t total_tokens, int32_t num_seqs,
+                                                   int32_t num_heads, int32_t head_dim,
+                                                   int32_t width, int32_t dtype) {
+    g_err[0] = 0;
+    const char* fn = "shortconv_kv_backward_workspace_size";
+    if (check_backward_shape(fn, total_tokens, num_seqs, num_heads, head_dim, width, dtype) !=
+        SC_OK)
+        return SIZE_MAX;
+    return sc::backward_shape(total_tokens, num_seqs, num_heads, head_dim, width, dtype)
+        .workspace_bytes;
+}
+
+SC_API int shortconv_kv_backward(
+    const void* k, const void* v, int64_t k_tok_stride, int64_t v_tok_stride,
+    const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens, const float* k_taps,
+    const float* v_taps, const float* k_gamma, const float* v_gamma, float eps, const void* k_state,
+    const void* v_state, int64_t num_state_slots, const int32_t* state_idx,
+    const uint8_t* has_initial_state, const void* dy_k, const void* dy_v, const void* dstate_out_k,
+    const void* dstate_out_v, void* dk, void* dv, float* dk_taps, float* dv_taps, float* dk_gamma,
+    float* dv_gamma, void* dstate_in_k, void* dstate_in_v, void* workspace,
+    size_t workspace_bytes, int32_t num_heads, int32_t head_dim, int32_t width, int32_t dtype,
+    void* stream) {
+    g_err[0] = 0;
+    const char* fn = "shortconv_kv_backward";
+    int rc = check_backward_shape(fn, total_tokens, num_seqs, num_heads, head_dim, width, dtype);
+    if (rc != SC_OK) return rc;
+    if (!k_taps || !v_taps || !k_gamma || !v_gamma)
+        return fail(SC_ERR_INVALID, "%s: null taps or gamma", fn);
+    if (!dk_taps || !dv_taps || !dk_gamma || !dv_gamma)
+        return fail(SC_ERR_INVALID, "%s: null taps or gamma gradient", fn);
+    if (total_tokens > 0 && (!k || !v)) return fail(SC_ERR_INVALID, "%s: null K or V input", fn);
+    if (total_tokens > 0 && (!dy_k || !dy_v))
+        return fail(SC_ERR_INVALID, "%s: null output gradient", fn);
+    if (total_tokens > 0 && (!dk || !dv)) return fail(SC_ERR_INVALID, "%s: null input gradient", fn);
+    if (num_seqs > 0 && !cu_seqlens) return fail(SC_ERR_INVALID, "%s: null cu_seqlens", fn);
+    if (num_state_slots < 0) return fail(SC_ERR_INVALID, "%s: num_state_slots < 0", fn);
+    if (width > 1 && num_state_slots > 0 && (!k_state || !v_state))
+        return fail(SC_ERR_INVALID, "%s: null conv state with width %d > 1", fn, width);
+    if (!dstate_out_k != !dstate_out_v)
+        return fail(SC_ERR_INVALID, "%s: new-state gradient given for one tensor only", fn);
+    if (!dstate_in_k != !dstate_in_v)
+        return fail(SC_ERR_INVALID, "%s: initial-state gradient requested for one tensor only", fn);
+    if (!(eps >= 0.0f) || eps > 3.0e38f)
+        return fail(SC_ERR_INVALID, "%s: eps must be finite and >= 0", fn);
+    const int64_t row = (int64_t)num_heads * head_dim;
+    const int eb = element_bytes(dtype);
+    if (k_tok_stride < row || v_tok_stride < row)
+        return fail(SC_ERR_INVALID, "%s: token stride smaller than num_heads*head_dim", fn);
+    if ((k_tok_stride * eb) % 16 || (v_tok_stride * eb) % 16)
+        return fail(SC_ERR_INVALID, "%s: token stride must be a multiple of 16 bytes", fn);
+    const void* ptrs[] = {k, v, k_taps, v_taps, k_gamma, v_gamma, k_state, v_state, dy_k, dy_v,
+                          dstate_out_k, dstate_out_v, dk, dv, dk_taps, dv_taps, dk_gamma,
+                          dv_gamma, dstate_in_k, dstate_in_v, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return fail(SC_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
+    const sc::BwdShape sh =
+        sc::backward_shape(total_tokens, num_seqs, num_heads, head_dim, width, dtype);
+    if (sh.workspace_bytes > 0 && (!workspace || workspace_bytes < sh.workspace_bytes))
+        return fail(SC_ERR_INVALID, "%s: workspace of %zu bytes needed, %zu given", fn,
+                    sh.workspace_bytes, workspace ? workspace_bytes : (size_t)0);
+
+    sc::BwdArgs a = {};
+    a.x[0] = k;
+    a.x[1] = v;
+    a.x_stride[0] = k_tok_stride;
+    a.x_stride[1] = v_tok_stride;
+    a.taps[0] = k_taps;
+    a.taps[1] = v_taps;
+    a.gamma[0] = k_gamma;
+    a.gamma[1] = v_gamma;
+    a.state[0] = width > 1 ? k_state : nullptr;
+    a.state[1] = width > 1 ? v_state : nullptr;
+    a.dy[0] = dy_k;
+    a.dy[1] = dy_v;
+    a.gs[0] = width > 1 ? dstate_out_k : nullptr;
+    a.gs[1] = width > 1 ? dstate_out_v : nullptr;
+    a.dx[0] = dk;
+    a.dx[1] = dv;
+    a.dstate[0] = width > 1 ? dstate_in_k : nullptr;
+    a.dstate[1] = width > 1 ? dstate_in_v : nullptr;
+    a.dtaps[0] = dk_taps;
+    a.dtaps[1] = dv_taps;
+    a.dgamma[0] = dk_gamma;
+    a.dgamma[1] = dv_gamma;
+    a.partial = static_cast<float*>(workspace);
+    a.chunk = reinterpret_cast<double*>(static_cast<char*>(workspace) + sh.partial_bytes);
+    a.cu = cu_seqlens;
+    a.state_idx = state_idx;
+    a.has_init = has_initial_state;
+    a.tokens = total_tokens;
+    a.num_state_slots = width > 1 ? num_state_slots : 0;
+    a.num_seqs = num_seqs;
+    a.heads = num_heads;
+    a.lanes_per_tensor = (int32_t)sh.lanes_per_tensor;
+    a.slices = (int32_t)sh.slices;
+    a.tiles = (int32_t)sh.tiles;
+    a.groups = num_seqs > 0 ? (int32_t)sh.groups : 0;  // no sequence: gradients of zero
+    a.chunks = num_seqs > 0 ? (int32_t)sh.chunks : 0;
+    a.eps = eps;
+    hipError_t e = sc::launch_backward(a, dtype, head_dim, width, (hipStream_t)stream);
     if (e != hipSuccess) return fail(SC_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return SC_OK;
 }

@@ -41,13 +41,14 @@
 #ifndef SHORTCONV_H
 #define SHORTCONV_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define SHORTCONV_ABI_VERSION 3
+#define SHORTCONV_ABI_VERSION 4
 
 typedef enum {
     SC_DTYPE_F32 = 0,  /* IEEE binary32 */
@@ -206,6 +207,64 @@ int shortconv_state_commit(const void* k_snap, const void* v_snap, int32_t max_t
                            void* v_state, int64_t num_state_slots, const int32_t* state_idx,
                            int32_t num_heads, int32_t head_dim, int32_t width, int32_t dtype,
                            void* stream);
+
+/*
+ * shortconv_kv_backward: the gradients of the prefill step, for training (the English news item's
+ * paragraph 3: the RL trainer runs the model with train/infer-consistent kernels). Training reads
+ * the step's output y = the rows shortconv_kv_prefill writes (slot_mapping = identity), so this
+ * takes the gradient of a loss with respect to y and returns the gradients with respect to every
+ * input of the step, by the chain rule through the definition at the top of this file:
+ *
+ *   chat = c / r, dchat = dy * gamma, proj = (1/D) sum_d dchat * chat, dc = (dchat - chat*proj) / r
+ *   d_gamma[d]    = sum over tokens and heads of dy * chat
+ *   d_taps[k,h,d] = sum over tokens p of dc[p] * window_p[k]
+ *   d_input row   = sum_k taps[k] * dc[of the token whose window holds that row at position k]
+ *                   (+ the new-state gradient, for the rows that become the new state)
+ *
+ * Inputs (as for shortconv_kv_prefill; the state pools are only read):
+ *  k, v, k/v_tok_stride, cu_seqlens, num_seqs, total_tokens, taps, gamma, eps, k/v_state,
+ *  num_state_slots, state_idx, has_initial_state
+ *                   the forward call's arguments: the initial windows are the ones that call used
+ *                   (so the state pools must hold the state from before that call).
+ *  dy_k, dy_v       [total_tokens][H][D] contiguous, element type `dtype`: dLoss/dy.
+ *  dstate_out_k/v   [num_seqs][W-1][H][D] contiguous, element type `dtype`: dLoss/d(new conv
+ *                   state of sequence s), for chunked training where the state feeds the next
+ *                   chunk; both NULL = no loss on the new state.
+ * Outputs (overwritten):
+ *  dk, dv           [total_tokens][H][D] contiguous, element type `dtype` (rounded once).
+ *  dk/dv_taps       fp32 [W][H][D];   dk/dv_gamma fp32 [D].
+ *  dstate_in_k/v    [num_seqs][W-1][H][D] contiguous, element type `dtype`: dLoss/d(initial
+ *                   window rows) of each sequence; zero for a sequence that started from zeros
+ *                   (has_initial_state = 0 or no state slot). Both NULL = not computed.
+ *                   Indexed by sequence, not by pool row; add into the pool's gradient as needed.
+ * Workspace: `workspace_bytes` >= shortconv_kv_backward_workspace_size(...) bytes of device
+ *  memory (16-byte aligned), scratch for the parameter-gradient partials; its contents on entry
+ *  do not matter and on exit are unspecified. Calls that share a workspace must be ordered.
+ * Numerics: fp32 arithmetic (the forward's c and r are recomputed the same way). d_taps and
+ *  d_gamma are deterministic: each workgroup sums at most 4 tiles of at most 64 tokens per lane
+ *  in fp32, its 4 waves in order, and a second kernel adds the workgroup partials in fp64 in a
+ *  fixed order, rounding once to fp32.
+ * With num_seqs == 0 the parameter gradients are zero and nothing else is written.
+ */
+int shortconv_kv_backward(const void* k, const void* v, int64_t k_tok_stride, int64_t v_tok_stride,
+                          const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                          const float* k_taps, const float* v_taps, const float* k_gamma,
+                          const float* v_gamma, float eps, const void* k_state,
+                          const void* v_state, int64_t num_state_slots, const int32_t* state_idx,
+                          const uint8_t* has_initial_state, const void* dy_k, const void* dy_v,
+                          const void* dstate_out_k, const void* dstate_out_v, void* dk, void* dv,
+                          float* dk_taps, float* dv_taps, float* dk_gamma, float* dv_gamma,
+                          void* dstate_in_k, void* dstate_in_v, void* workspace,
+                          size_t workspace_bytes, int32_t num_heads, int32_t head_dim,
+                          int32_t width, int32_t dtype, void* stream);
+
+/*
+ * Bytes of workspace shortconv_kv_backward needs for these sizes (a host-side computation, no
+ * device access). SIZE_MAX when the sizes are invalid (shortconv_last_error() says why).
+ */
+size_t shortconv_kv_backward_workspace_size(int64_t total_tokens, int32_t num_seqs,
+                                            int32_t num_heads, int32_t head_dim, int32_t width,
+                                            int32_t dtype);
 
 /* Message for the last non-zero return on the calling thread ("" if none). Valid until the next
  * call on the same thread. */

@@ -45,8 +45,8 @@ def _bind(lib):
                                      ctypes.c_float, P, I64, P, P, P, P, ctypes.c_int]
     lib.sc_oracle_backward.restype = ctypes.c_int
     lib.sc_oracle_backward.argtypes = [ctypes.c_int, I64, I64, I64, I64, P, P, I64, P, P,
-                                       ctypes.c_float, P, I64, P, P, P, P, P, P, P, P,
-                                       ctypes.c_int]
+                                       ctypes.c_float, P, I64, P, P, P, P, P, P, P, P, P, P, P,
+                                       P, ctypes.c_int]
     return lib
 
 
@@ -238,10 +238,15 @@ class Grads:
     dtaps: np.ndarray
     dgamma: np.ndarray
     dstate: Optional[np.ndarray]
+    # error scales of an fp32 evaluation (see the C source), when asked for
+    cond_dx: Optional[np.ndarray] = None
+    cond_dtaps: Optional[np.ndarray] = None
+    cond_dgamma: Optional[np.ndarray] = None
+    cond_dstate: Optional[np.ndarray] = None
 
 
 def backward_one(x, cu_seqlens, taps, gamma, eps, state, state_idx, has_init, g, gs=None, *,
-                 nthreads=1):
+                 cond=False, nthreads=1):
     """Backward of ``prefill_one`` for the loss whose gradient is ``g`` = dLoss/dy (fp64
     [T,H,D]) plus ``gs`` = dLoss/d(new state) (fp64 [N,W-1,H,D] or None). The chain rule through
     the definition; the C source states each step."""
@@ -274,22 +279,27 @@ def backward_one(x, cu_seqlens, taps, gamma, eps, state, state_idx, has_init, g,
     dtaps = np.zeros((W, H, D), np.float64)
     dgamma = np.zeros(D, np.float64)
     dstate = np.zeros((N, W - 1, H, D), np.float64) if W > 1 else None
+    if cond:
+        cdx, cdt, cdg = np.zeros_like(dx), np.zeros_like(dtaps), np.zeros_like(dgamma)
+        cds = np.zeros_like(dstate) if dstate is not None else None
+    else:
+        cdx = cdt = cdg = cds = None
     rc = lib.sc_oracle_backward(code, H, D, W, N, _ptr(cu), _ptr(x), xs, _ptr(taps), _ptr(gamma),
                                 float(eps), _ptr(state), n_state, _ptr(sidx), _ptr(hinit), _ptr(g),
                                 _ptr(gs), _ptr(dx), _ptr(dtaps), _ptr(dgamma), _ptr(dstate),
-                                int(nthreads))
+                                _ptr(cdx), _ptr(cdt), _ptr(cdg), _ptr(cds), int(nthreads))
     if rc != 0:
         raise ValueError("oracle backward rejected its arguments")
-    return Grads(dx, dtaps, dgamma, dstate)
+    return Grads(dx, dtaps, dgamma, dstate, cdx, cdt, cdg, cds)
 
 
 def fused_backward(k, v, cu_seqlens, k_taps, v_taps, k_gamma, v_gamma, eps, k_state, v_state,
-                   state_idx, has_init, gk, gv, gsk=None, gsv=None, *, nthreads=1):
+                   state_idx, has_init, gk, gv, gsk=None, gsv=None, *, cond=False, nthreads=1):
     """``backward_one`` for K and V: returns (Grads of K, Grads of V)."""
     a = backward_one(k, cu_seqlens, k_taps, k_gamma, eps, k_state, state_idx, has_init, gk, gsk,
-                     nthreads=nthreads)
+                     cond=cond, nthreads=nthreads)
     b = backward_one(v, cu_seqlens, v_taps, v_gamma, eps, v_state, state_idx, has_init, gv, gsv,
-                     nthreads=nthreads)
+                     cond=cond, nthreads=nthreads)
     return a, b
 
 

@@ -255,6 +255,13 @@ int sc_oracle_decode(int dtype, int64_t H, int64_t D, int64_t W, int64_t B, cons
  *  dx         out fp64 [T][H][D]
  *  dtaps      out fp64 [W][H][D];   dgamma out fp64 [D]
  *  dstate     out fp64 [n_seq][W-1][H][D] or NULL
+ *  cond_*     out fp64, shaped like dx / dtaps / dgamma / dstate, or NULL: the scale of the
+ *             rounding error an fp32 evaluation of these formulas can carry (first order): per
+ *             token, with A[d] = sum_k |taps[k] e[p+k]| (which bounds the error of c),
+ *               M[p,d] = (|dchat| + (A/r) |proj| + |chat| (P1 + P2)) / r,
+ *               P1 = (1/D) sum_j |dchat_j chat_j|,  P2 = (1/D) sum_j |dchat_j| A_j / r;
+ *             cond_dx = sum_k |taps[k]| M[i-k] (+ |gs|), cond_dtaps = sum_p (M + |dc|) |e[p+k]|,
+ *             cond_dgamma = sum |g| (|chat| + A/r).
  *
  * The sums over sequences (dtaps) and over sequences and heads (dgamma) are taken per
  * (sequence, head) unit first and then added in unit order, so the result does not depend on the
@@ -265,7 +272,8 @@ int sc_oracle_backward(int dtype, int64_t H, int64_t D, int64_t W, int64_t n_seq
                        const float* gamma, float eps, const void* state, int64_t n_state,
                        const int64_t* state_idx, const uint8_t* has_init, const double* g,
                        const double* gs, double* dx, double* dtaps, double* dgamma,
-                       double* dstate, int nthreads)
+                       double* dstate, double* cond_dx, double* cond_dtaps, double* cond_dgamma,
+                       double* cond_dstate, int nthreads)
 {
     if (H <= 0 || D <= 0 || W <= 0 || n_seq < 0 || x_stride < H * D) return -1;
     if (dtype != ORC_F32 && dtype != ORC_BF16) return -1;
@@ -273,6 +281,8 @@ int sc_oracle_backward(int dtype, int64_t H, int64_t D, int64_t W, int64_t n_seq
     const int64_t units = n_seq * H;
     double* part_taps = (double*)calloc((size_t)(units > 0 ? units : 1) * W * D, sizeof(double));
     double* part_gamma = (double*)calloc((size_t)(units > 0 ? units : 1) * D, sizeof(double));
+    double* part_ctaps = (double*)calloc((size_t)(units > 0 ? units : 1) * W * D, sizeof(double));
+    double* part_cgamma = (double*)calloc((size_t)(units > 0 ? units : 1) * D, sizeof(double));
     (void)nthreads;
 
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
@@ -284,9 +294,13 @@ int sc_oracle_backward(int dtype, int64_t H, int64_t D, int64_t W, int64_t n_seq
         const int64_t E = R + L; /* rows of e */
         double* e = (double*)malloc((size_t)(E > 0 ? E : 1) * D * sizeof(double));
         double* dc = (double*)malloc((size_t)(L > 0 ? L : 1) * D * sizeof(double));
+        double* mg = (double*)malloc((size_t)(L > 0 ? L : 1) * D * sizeof(double));
         double* c = (double*)malloc((size_t)D * sizeof(double));
+        double* av = (double*)malloc((size_t)D * sizeof(double));
         double* pt = part_taps + u * W * D;
         double* pg = part_gamma + u * D;
+        double* pct = part_ctaps + u * W * D;
+        double* pcg = part_cgamma + u * D;
 
         /* the window rows e[0 .. R+L) of this sequence and head */
         for (int64_t i = 0; i < E; ++i)
@@ -300,10 +314,13 @@ int sc_oracle_backward(int dtype, int64_t H, int64_t D, int64_t W, int64_t n_seq
             /* forward quantities of token p */
             double sumsq = 0.0;
             for (int64_t d = 0; d < D; ++d) {
-                double acc = 0.0;
-                for (int64_t k = 0; k < W; ++k)
+                double acc = 0.0, mag = 0.0;
+                for (int64_t k = 0; k < W; ++k) {
                     acc += (double)taps[(k * H + h) * D + d] * e[(p + k) * D + d];
+                    mag += fabs((double)taps[(k * H + h) * D + d] * e[(p + k) * D + d]);
+                }
                 c[d] = acc;
+                av[d] = mag;
                 sumsq += acc * acc;
             }
             const double rp = sqrt(sumsq / (double)D + (double)eps);
@@ -325,41 +342,73 @@ int sc_oracle_backward(int dtype, int64_t H, int64_t D, int64_t W, int64_t n_seq
             for (int64_t k = 0; k < W; ++k)
                 for (int64_t d = 0; d < D; ++d)
                     pt[k * D + d] += dc[p * D + d] * e[(p + k) * D + d];
+            /* error scales (first-order model of an fp32 evaluation) */
+            double p1 = 0.0, p2 = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                const double dch = fabs(g[((start + p) * H + h) * D + d] * (double)gamma[d]);
+                p1 += dch * fabs(c[d] / rp);
+                p2 += dch * av[d] / rp;
+            }
+            p1 /= (double)D;
+            p2 /= (double)D;
+            for (int64_t d = 0; d < D; ++d) {
+                const double gd = g[((start + p) * H + h) * D + d];
+                const double chat = fabs(c[d] / rp);
+                mg[p * D + d] = (fabs(gd * (double)gamma[d]) + av[d] / rp * fabs(proj) +
+                                 chat * (p1 + p2)) / rp;
+                pcg[d] += fabs(gd) * (chat + av[d] / rp);
+                for (int64_t k = 0; k < W; ++k)
+                    pct[k * D + d] += (mg[p * D + d] + fabs(dc[p * D + d])) *
+                                      fabs(e[(p + k) * D + d]);
+            }
         }
 
         /* through the convolution: its input rows, plus the loss on the new state */
         for (int64_t i = 0; i < E; ++i) {
             for (int64_t d = 0; d < D; ++d) {
-                double acc = 0.0;
+                double acc = 0.0, cnd = 0.0;
                 for (int64_t k = 0; k < W; ++k) {
                     const int64_t p = i - k;
                     if (p >= 0 && p < L) acc += (double)taps[(k * H + h) * D + d] * dc[p * D + d];
+                    if (p >= 0 && p < L) cnd += fabs((double)taps[(k * H + h) * D + d]) * mg[p * D + d];
                 }
                 if (gs && i >= L) acc += gs[((s * R + (i - L)) * H + h) * D + d];
-                if (i >= R)
+                if (gs && i >= L) cnd += fabs(gs[((s * R + (i - L)) * H + h) * D + d]);
+                if (i >= R) {
                     dx[((start + i - R) * H + h) * D + d] = acc;
-                else if (dstate)
-                    dstate[((s * R + i) * H + h) * D + d] = from_state ? acc : 0.0;
+                    if (cond_dx) cond_dx[((start + i - R) * H + h) * D + d] = cnd;
+                } else {
+                    if (dstate) dstate[((s * R + i) * H + h) * D + d] = from_state ? acc : 0.0;
+                    if (cond_dstate) cond_dstate[((s * R + i) * H + h) * D + d] = from_state ? cnd : 0.0;
+                }
             }
         }
         free(e);
         free(dc);
+        free(mg);
         free(c);
+        free(av);
     }
 
     for (int64_t k = 0; k < W; ++k)
         for (int64_t h = 0; h < H; ++h)
             for (int64_t d = 0; d < D; ++d) {
-                double acc = 0.0;
+                double acc = 0.0, cnd = 0.0;
                 for (int64_t s = 0; s < n_seq; ++s) acc += part_taps[((s * H + h) * W + k) * D + d];
+                for (int64_t s = 0; s < n_seq; ++s) cnd += part_ctaps[((s * H + h) * W + k) * D + d];
                 dtaps[(k * H + h) * D + d] = acc;
+                if (cond_dtaps) cond_dtaps[(k * H + h) * D + d] = cnd;
             }
     for (int64_t d = 0; d < D; ++d) {
-        double acc = 0.0;
+        double acc = 0.0, cnd = 0.0;
         for (int64_t u = 0; u < units; ++u) acc += part_gamma[u * D + d];
+        for (int64_t u = 0; u < units; ++u) cnd += part_cgamma[u * D + d];
         dgamma[d] = acc;
+        if (cond_dgamma) cond_dgamma[d] = cnd;
     }
     free(part_taps);
     free(part_gamma);
+    free(part_ctaps);
+    free(part_cgamma);
     return 0;
 }

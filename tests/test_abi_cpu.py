@@ -30,7 +30,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["shortconv_abi_version", "shortconv_kv_decode",
+    assert declared_functions() == ["shortconv_abi_version", "shortconv_kv_backward",
+                                    "shortconv_kv_backward_workspace_size", "shortconv_kv_decode",
                                     "shortconv_kv_decode_mxfp8", "shortconv_kv_prefill",
                                     "shortconv_kv_prefill_mxfp8", "shortconv_kv_verify",
                                     "shortconv_last_error", "shortconv_mxfp8_quantize",
@@ -159,3 +160,63 @@ def test_python_binding_fails_loudly_without_library(tmp_path):
             _binding.load_library(str(tmp_path / "missing.so"))
     finally:
         _binding._lib = saved
+
+
+def backward_args(**over):
+    a = dict(k=FAKE, v=FAKE, ks=1024, vs=1024, cu=FAKE, n=2, T=10, kt=FAKE, vt=FAKE, kg=FAKE,
+             vg=FAKE, eps=1e-6, kst=FAKE, vst=FAKE, S=2, sidx=FAKE, hinit=FAKE, dyk=FAKE,
+             dyv=FAKE, gsk=None, gsv=None, dk=FAKE, dv=FAKE, dkt=FAKE, dvt=FAKE, dkg=FAKE,
+             dvg=FAKE, dsk=None, dsv=None, ws=FAKE, wsb=1 << 40, H=8, D=128, W=4, dtype=1,
+             stream=None)
+    a.update(over)
+    return [a[k] for k in ("k", "v", "ks", "vs", "cu", "n", "T", "kt", "vt", "kg", "vg", "eps",
+                           "kst", "vst", "S", "sidx", "hinit", "dyk", "dyv", "gsk", "gsv", "dk",
+                           "dv", "dkt", "dvt", "dkg", "dvg", "dsk", "dsv", "ws", "wsb", "H", "D",
+                           "W", "dtype", "stream")]
+
+
+BACKWARD_CASES = [
+    (dict(dtype=3), UNSUPPORTED, "dtype"),
+    (dict(D=32), UNSUPPORTED, "head_dim"),
+    (dict(W=9), UNSUPPORTED, "width"),
+    (dict(H=0), INVALID, "num_heads"),
+    (dict(n=-1), INVALID, "num_seqs"),
+    (dict(T=1 << 31), INVALID, "total_tokens"),
+    (dict(kt=None), INVALID, "taps or gamma"),
+    (dict(dvg=None), INVALID, "gradient"),
+    (dict(dyk=None), INVALID, "output gradient"),
+    (dict(dv=None), INVALID, "input gradient"),
+    (dict(cu=None), INVALID, "cu_seqlens"),
+    (dict(vst=None), INVALID, "conv state"),
+    (dict(gsk=FAKE), INVALID, "new-state gradient"),
+    (dict(dsv=FAKE), INVALID, "initial-state gradient"),
+    (dict(eps=float("inf")), INVALID, "eps"),
+    (dict(ks=100), INVALID, "stride"),
+    (dict(dk=FAKE + 4), INVALID, "aligned"),
+    (dict(ws=None), INVALID, "workspace"),
+    (dict(wsb=16), INVALID, "workspace"),
+]
+
+
+@pytest.mark.parametrize("over,code,msg", BACKWARD_CASES, ids=[c[2] + str(i) for i, c in
+                                                               enumerate(BACKWARD_CASES)])
+def test_backward_rejects(lib, over, code, msg):
+    from causal_short_convolution_amd import _binding
+    _binding.load_library()
+    rc = lib.shortconv_kv_backward(*backward_args(**over))
+    assert rc == code
+    err = lib.shortconv_last_error().decode()
+    assert err.startswith("shortconv_kv_backward") and msg in err, err
+
+
+def test_backward_workspace_size(lib):
+    from causal_short_convolution_amd import _binding
+    _binding.load_library()  # sets the ctypes signatures
+    size = lib.shortconv_kv_backward_workspace_size
+    # bf16, H=8, D=128, W=4: 256 lanes per tensor -> 8 slices of 64; tiles of 4 waves x 16 tokens:
+    # 17060 // 64 + 8 = 274 tiles -> 69 groups of 4 tiles; an fp32 partial of (W + 1) * 64 lanes
+    # * 4 channels per slice and group, then fp64 sums of chunks of 64 groups (2 chunks)
+    assert size(17060, 8, 8, 128, 4, 1) == 69 * 8 * 5 * 256 * 4 + 2 * 8 * 5 * 256 * 8
+    assert size(0, 0, 8, 128, 4, 1) == 0
+    assert size(10, 2, 8, 96, 4, 1) == 2 ** 64 - 1  # unsupported head_dim -> SIZE_MAX
+    assert "head_dim" in lib.shortconv_last_error().decode()

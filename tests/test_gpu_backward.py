@@ -1,0 +1,216 @@
+"""GPU parity of the backward (shortconv_kv_backward) against the fp64 oracle's backward.
+
+Judging rule: an element passes when |got - exact| <= tol*|exact| + K * 2^-24 * cond, with cond
+the oracle's first-order error scale of an fp32 evaluation (oracle/shortconv_oracle.c, backward),
+tol = 1e-5 for fp32 outputs and 3.9e-3 (one bf16 ulp) for bf16 outputs, K = 64 for the row
+gradients (dx, initial-window gradient) and 96 for the parameter gradients: each product carries
+dc's row-level error (64 units of M) and the kernel adds each lane's products over at most 64
+tokens in fp32, then 4 waves, then the workgroup partials in fp64, so at most 68 roundings of
+sum(|terms|) on top -- 68 * 2^-24 * sum((M + |dc|) |e|), with margin. Rows that the call must not
+write keep their sentinel; the tap and gamma gradients are bit-identical across runs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_harness import DEV, ORACLE_THREADS, TORCH_DT, rows_to_dev, to_dev, to_host
+from causal_short_convolution_amd import (ShortConvError, shortconv_kv_backward,
+                                          shortconv_kv_backward_workspace_size)
+
+pytestmark = pytest.mark.gpu
+
+K_ROWS = 64.0
+K_PARAMS = 96.0
+TOL = {"f32": 1e-5, "bf16": 3.9e-3}
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _stored_normal(g, shape, dtype):
+    f = g.standard_normal(shape, dtype=np.float32)
+    return f if dtype == "f32" else workloads.to_bf16_bits(f)
+
+
+def _judge(name, got, exact, cond, tol, K):
+    g = oracle.widen(got) if got.dtype in (np.uint16, np.float32) else got.astype(np.float64)
+    err = np.abs(g - exact)
+    bound = tol * np.abs(exact) + K * 2.0 ** -24 * cond
+    assert np.isfinite(g).all(), f"{name}: non-finite values"
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, err / bound, np.where(err > 0, np.inf, 0.0))
+    worst = float(ratio.max()) if ratio.size else 0.0
+    at = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert worst <= 1.0, f"{name}: worst error / bound = {worst:.3g} at {at}"
+    return worst
+
+
+class BwdCase:
+    def __init__(self, dtype, H, D, W, lens, hin, seed, gs=True, dstate=True, eps=None,
+                 token_pad=0, spec=None):
+        if spec is None:
+            spec = workloads.Spec(dtype=dtype, H=H, D=D, W=W, seed=seed, prefill_lens=list(lens),
+                                  has_init=list(hin), token_pad=token_pad)
+            if eps is not None:
+                spec.eps = eps
+        self.w = w = workloads.build(spec)
+        self.st = st = w.steps[0]
+        self.dtype, self.H, self.D, self.W = w.dtype, w.H, w.D, w.W
+        R = w.W - 1
+        N, T = st.num_seqs, st.tokens
+        g = np.random.default_rng(1000 + spec.seed)
+        self.dyk = _stored_normal(g, (T, w.H, w.D), w.dtype)
+        self.dyv = _stored_normal(g, (T, w.H, w.D), w.dtype)
+        self.gsk = _stored_normal(g, (N, R, w.H, w.D), w.dtype) if (gs and R > 0) else None
+        self.gsv = _stored_normal(g, (N, R, w.H, w.D), w.dtype) if (gs and R > 0) else None
+        self.want_dstate = dstate and R > 0
+
+    def run_gpu(self):
+        w, st = self.w, self.st
+        R, N, T = self.W - 1, st.num_seqs, st.tokens
+        dt = TORCH_DT[self.dtype]
+        bits = torch.int32 if self.dtype == "f32" else torch.int16
+        sentinel = 0x5A5A5A5A if self.dtype == "f32" else 0x5A5A
+
+        def filled(shape):
+            t = torch.empty(shape, dtype=dt, device=DEV)
+            t.view(bits).fill_(sentinel)
+            return t
+
+        dk, dv = filled((T, self.H, self.D)), filled((T, self.H, self.D))
+        dks = dvs = None
+        if self.want_dstate:
+            dks, dvs = filled((N, R, self.H, self.D)), filled((N, R, self.H, self.D))
+        dkt = torch.full((self.W, self.H, self.D), float("nan"), device=DEV)
+        dvt = torch.full_like(dkt, float("nan"))
+        dkg = torch.full((self.D,), float("nan"), device=DEV)
+        dvg = torch.full_like(dkg, float("nan"))
+        shortconv_kv_backward(
+            rows_to_dev(st.k), rows_to_dev(st.v), to_dev(st.cu_seqlens.astype(np.int32)),
+            to_dev(w.k_taps), to_dev(w.v_taps), to_dev(w.k_gamma), to_dev(w.v_gamma), w.eps,
+            to_dev(w.k_state), to_dev(w.v_state), to_dev(st.state_idx.astype(np.int32)),
+            to_dev(st.has_init.astype(np.uint8)), to_dev(self.dyk), to_dev(self.dyv), dk, dv,
+            dkt, dvt, dkg, dvg, dstate_out=(to_dev(self.gsk), to_dev(self.gsv)),
+            dstate_in=(dks, dvs))
+        torch.cuda.synchronize()
+        out = dict(dk=to_host(dk, self.dtype), dv=to_host(dv, self.dtype),
+                   dkt=dkt.cpu().numpy(), dvt=dvt.cpu().numpy(), dkg=dkg.cpu().numpy(),
+                   dvg=dvg.cpu().numpy())
+        if self.want_dstate:
+            out["dks"] = to_host(dks, self.dtype)
+            out["dvs"] = to_host(dvs, self.dtype)
+        return out
+
+    def oracle(self):
+        w, st = self.w, self.st
+        wid = oracle.widen
+        return oracle.fused_backward(
+            st.k, st.v, st.cu_seqlens, w.k_taps, w.v_taps, w.k_gamma, w.v_gamma, w.eps, w.k_state,
+            w.v_state, st.state_idx, st.has_init, wid(self.dyk), wid(self.dyv),
+            None if self.gsk is None else wid(self.gsk),
+            None if self.gsv is None else wid(self.gsv), cond=True, nthreads=ORACLE_THREADS)
+
+    def check(self, got=None):
+        got = self.run_gpu() if got is None else got
+        gk, gv = self.oracle()
+        tol = TOL[self.dtype]
+        worst = {}
+        for t, gr in (("k", gk), ("v", gv)):
+            worst["d" + t] = _judge(f"d{t}", got["d" + t], gr.dx, gr.cond_dx, tol, K_ROWS)
+            worst["d" + t + "_taps"] = _judge(f"d{t}_taps", got["d" + t + "t"], gr.dtaps,
+                                              gr.cond_dtaps, 1e-5, K_PARAMS)
+            worst["d" + t + "_gamma"] = _judge(f"d{t}_gamma", got["d" + t + "g"], gr.dgamma,
+                                               gr.cond_dgamma, 1e-5, K_PARAMS)
+            if self.want_dstate:
+                worst["d" + t + "_state"] = _judge(f"d{t}_state", got["d" + t + "s"], gr.dstate,
+                                                   gr.cond_dstate, tol, K_ROWS)
+        return worst
+
+
+SHAPES = [
+    # dtype, H, D, W, lens, has_init
+    ("bf16", 8, 128, 4, [100, 1, 0, 17, 64, 3], [1, 0, 1, 1, 0, 1]),
+    ("bf16", 2, 64, 8, [40, 5, 0, 130, 7], [1, 1, 0, 1, 1]),
+    ("bf16", 1, 256, 2, [9, 33, 1], [0, 1, 1]),
+    ("bf16", 3, 128, 1, [20, 0, 7], [1, 1, 0]),
+    ("f32", 1, 64, 4, [64, 2, 19], [0, 1, 1]),
+    ("f32", 4, 128, 8, [30, 6, 71], [1, 0, 1]),
+    ("f32", 2, 256, 3, [2, 50, 0, 13], [1, 1, 1, 0]),
+    ("bf16", 16, 128, 6, [200, 3], [1, 1]),
+]
+
+
+@pytest.mark.parametrize("dtype,H,D,W,lens,hin", SHAPES,
+                         ids=[f"{s[0]}-H{s[1]}-D{s[2]}-W{s[3]}" for s in SHAPES])
+def test_backward_matches_oracle(dtype, H, D, W, lens, hin):
+    case = BwdCase(dtype, H, D, W, lens, hin, seed=7 + W + H)
+    case.check()
+
+
+@pytest.mark.parametrize("gs,dstate", [(False, True), (True, False), (False, False)])
+def test_backward_optional_state_gradients(gs, dstate):
+    case = BwdCase("bf16", 4, 128, 4, [15, 2, 0, 40], [1, 1, 1, 0], seed=3, gs=gs, dstate=dstate)
+    case.check()
+
+
+def test_backward_token_strided_inputs_and_eps_zero():
+    case = BwdCase("f32", 2, 64, 4, [33, 1, 12], [1, 0, 1], seed=9, token_pad=12, eps=0.0)
+    case.check()
+
+
+def test_backward_is_deterministic():
+    case = BwdCase("bf16", 8, 128, 4, [500, 37, 260], [1, 0, 1], seed=11)
+    a = case.run_gpu()
+    b = case.run_gpu()
+    for key in a:
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+    case.check(a)
+
+
+@pytest.mark.parametrize("n", [2, 4])
+def test_backward_reference_workload_shapes(n):
+    """The varlen prefill and long prefill workloads, at full size."""
+    spec = workloads.config_spec(n)
+    case = BwdCase(None, None, None, None, None, None, seed=None, spec=spec)
+    worst = case.check()
+    print(f"config {n} backward worst error/bound: {worst}")
+
+
+def test_backward_without_sequences_zeroes_parameter_gradients():
+    H, D, W = 2, 64, 4
+    dkt = torch.full((W, H, D), float("nan"), device=DEV)
+    dvt = torch.full_like(dkt, 1.0)
+    dkg, dvg = torch.full((D,), 2.0, device=DEV), torch.full((D,), 3.0, device=DEV)
+    taps = torch.zeros((W, H, D), device=DEV)
+    gam = torch.ones(D, device=DEV)
+    empty = torch.zeros((0, H, D), dtype=torch.bfloat16, device=DEV)
+    shortconv_kv_backward(empty, empty, torch.zeros(1, dtype=torch.int32, device=DEV), taps, taps,
+                          gam, gam, 1e-6, None, None, None, None, empty, empty, empty, empty,
+                          dkt, dvt, dkg, dvg)
+    torch.cuda.synchronize()
+    for t in (dkt, dvt, dkg, dvg):
+        assert (t == 0).all()
+
+
+def test_backward_rejects_short_workspace():
+    case = BwdCase("bf16", 8, 128, 4, [50, 3], [1, 1], seed=2)
+    w, st = case.w, case.st
+    need = shortconv_kv_backward_workspace_size(st.tokens, st.num_seqs, 8, 128, 4, torch.bfloat16)
+    assert need > 0
+    ws = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
+    dk = torch.empty((st.tokens, 8, 128), dtype=torch.bfloat16, device=DEV)
+    g = torch.empty((4, 8, 128), device=DEV)
+    gm = torch.empty(128, device=DEV)
+    with pytest.raises(ShortConvError, match="workspace"):
+        shortconv_kv_backward(rows_to_dev(st.k), rows_to_dev(st.v),
+                              to_dev(st.cu_seqlens.astype(np.int32)), to_dev(w.k_taps),
+                              to_dev(w.v_taps), to_dev(w.k_gamma), to_dev(w.v_gamma), w.eps,
+                              to_dev(w.k_state), to_dev(w.v_state),
+                              to_dev(st.state_idx.astype(np.int32)),
+                              to_dev(st.has_init.astype(np.uint8)), dk, dk, dk.clone(), dk.clone(),
+                              g, g.clone(), gm, gm.clone(), workspace=ws)
