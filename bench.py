@@ -43,8 +43,7 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_varlen_bf16_traffic.md
 WORKLOADS = {"tiny_ref": 1, "varlen_prefill": 2, "decode": 3, "long_prefill": 4, "mixed": 5}
 COPY_BYTES = 512 << 20          # calibration copy: 512 MiB read + 512 MiB written
 KERNELS = ("prefill_kernel", "decode_kernel", "verify_kernel", "commit_kernel",
-           "mx_quantize_kernel", "backward_kernel", "backward_chunk_kernel", "backward_taps_kernel",
-           "backward_gamma_kernel")
+           "mx_quantize_kernel", "backward_kernel", "backward_chunk_kernel", "backward_final_kernel")
 
 
 def kernel_source_sha():

@@ -478,6 +478,7 @@ SC_API int shortconv_kv_backward(
     a.tiles = (int32_t)sh.tiles;
     a.groups = num_seqs > 0 ? (int32_t)sh.groups : 0;  // no sequence: gradients of zero
     a.chunks = num_seqs > 0 ? (int32_t)sh.chunks : 0;
+    a.tiles_per_group = (int32_t)sh.tiles_per_group;
     a.eps = eps;
     hipError_t e = sc::launch_backward(a, dtype, head_dim, width, (hipStream_t)stream);
     if (e != hipSuccess) return fail(SC_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));

@@ -19,8 +19,9 @@
 // within the register file. A wave covers one 64-lane column slice of the K|V rows.
 //
 // Grid: the forward's per-sequence tiles (4 waves x BT tokens of one sequence, found by the same
-// wave-parallel search); each workgroup walks kTilesPerGroup consecutive tiles of its column
-// slice, so that each lane's fp32 sums of the tap and gamma gradients stay short. Per tile a wave:
+// wave-parallel search); each workgroup walks up to 4 consecutive tiles of its column slice
+// (fewer when the problem is too small to fill the chip otherwise), so that each lane's fp32 sums
+// of the tap and gamma gradients stay short. Per tile a wave:
 //   phase 1: loads its W-1 halo rows, its BT input rows and BT gradient rows in one burst, then
 //            for each token computes dc, accumulates the parameter gradients and emits the input
 //            gradient of every token whose dc window (the token and the W-1 after it) lies inside
@@ -40,7 +41,10 @@ namespace {
 
 constexpr int kBwdBlock = 256;
 constexpr int kBwdWaves = kBwdBlock / 64;
-constexpr int kTilesPerGroup = 4;  // tiles a workgroup walks (bounds each fp32 partial's length)
+// Tiles a workgroup walks: at most kMaxTilesPerGroup (bounds each fp32 partial's length), and
+// fewer when that leaves too few workgroups to fill the chip (kFillBlocks).
+constexpr int kMaxTilesPerGroup = 4;
+constexpr int64_t kFillBlocks = 2048;
 
 // Span tokens per wave: a span's input and gradient rows are all in flight at once, so wide
 // windows and fp32 rows take shorter spans to stay within the register file. Tuning knobs
@@ -52,15 +56,15 @@ constexpr int kTilesPerGroup = 4;  // tiles a workgroup walks (bounds each fp32 
 #define SC_BWD_BT_BF16_WIDE 8   // bf16, W > 5
 #endif
 #ifndef SC_BWD_BT_F32
-#define SC_BWD_BT_F32 16        // fp32, W <= 3
+#define SC_BWD_BT_F32 16        // fp32, W == 1
 #endif
 #ifndef SC_BWD_BT_F32_WIDE
-#define SC_BWD_BT_F32_WIDE 8    // fp32, W > 3
+#define SC_BWD_BT_F32_WIDE 8    // fp32, W > 1
 #endif
 template <class E, int W>
 constexpr int bwd_span() {
     return E::BYTES == 2 ? (W <= 5 ? SC_BWD_BT_BF16 : SC_BWD_BT_BF16_WIDE)
-                         : (W <= 3 ? SC_BWD_BT_F32 : SC_BWD_BT_F32_WIDE);
+                         : (W <= 1 ? SC_BWD_BT_F32 : SC_BWD_BT_F32_WIDE);
 }
 
 // 4 channels of one lane, in the I/O element type, with streaming (non-temporal) access.
@@ -238,8 +242,8 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
     }
 
 #pragma unroll 1
-    for (int gi = 0; gi < kTilesPerGroup; ++gi) {
-        const int64_t tile = (int64_t)group * kTilesPerGroup + gi;
+    for (int gi = 0; gi < a.tiles_per_group; ++gi) {
+        const int64_t tile = (int64_t)group * a.tiles_per_group + gi;
         if (tile >= a.tiles) break;  // the same for the whole workgroup
         const int s = find_tile_seq<BB>(a.cu, a.num_seqs, T, tile);
         const int64_t start = uniform((int64_t)clamp_tok(a.cu[s], T));
@@ -276,7 +280,14 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
                                : from_state ? state + (int64_t)idx * R * row_bytes
                                             : reinterpret_cast<const char*>(taps_p);
             const int64_t hstride = !first_span ? xs : row_bytes;
+            // Loads, oldest first: the new-state loss rows (only in a span holding some of the
+            // sequence's last R rows; being the oldest, the branch around them does not hide from
+            // the compiler which later loads are still in flight), the halo, then the rows.
             Raw halo[RR], xr[BT], gr[BT];
+            if (has_tail) {
+#pragma unroll
+                for (int m = 0; m < R; ++m) gsr[m] = Q::load(gs_seq + m * row_bytes + lane_off);
+            }
 #pragma unroll
             for (int k = 0; k < R; ++k) halo[k] = Q::load(hsrc + k * hstride + lane_off);
             const int last = n - 1;
@@ -286,11 +297,6 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
                 xr[i] = Q::load(x + (t0 + r) * xs + lane_off);
                 gr[i] = Q::load(dy + (t0 + r) * row_bytes + lane_off);
             }
-            if (has_tail) {
-#pragma unroll
-                for (int m = 0; m < R; ++m) gsr[m] = Q::load(gs_seq + m * row_bytes + lane_off);
-            }
-            wait_vmem();
             if (first_span && !from_state) {
 #pragma unroll
                 for (int k = 0; k < R; ++k) halo[k] = Q::zero();
@@ -302,6 +308,11 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) dcr[k][v] = 0.0f;
 
+            // The tokens issue no store (their results stay in registers until the loop ends), so
+            // the compiler waits for each token's rows alone and the first tokens are computed
+            // while later rows arrive; a store among them would make it wait for everything.
+            Raw dx_out[BT - R > 0 ? BT - R : 1];
+            Raw ds_out[RR];
 #pragma unroll
             for (int i = 0; i < BT; ++i) {
                 float dci[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -339,9 +350,7 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
 #pragma unroll
                             for (int v = 0; v < 4; ++v) de[v] = 0.0f;
                         }
-                        if (active)
-                            Q::store(dstate + ((int64_t)s * R + m) * row_bytes + lane_off,
-                                     Q::narrow(de));
+                        ds_out[m] = Q::narrow(de);
                     }
                 }
                 // rows whose dc window lies inside the span: q = i - R
@@ -350,8 +359,18 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
                     float de[4];
                     row_grad<W>(tap, dcr, q, de);
                     if (has_tail) add_state_loss<E, R>(gsr, p0 + q - (L - R), de);
-                    if (active) Q::store(dx + (t0 + q) * row_bytes + lane_off, Q::narrow(de));
+                    dx_out[q] = Q::narrow(de);
                 }
+            }
+            if (R > 0 && first_span && dstate != nullptr && active) {
+#pragma unroll
+                for (int m = 0; m < R; ++m)
+                    Q::store(dstate + ((int64_t)s * R + m) * row_bytes + lane_off, ds_out[m]);
+            }
+            if (active) {
+#pragma unroll
+                for (int q = 0; q < BT - R; ++q)
+                    if (q < n) Q::store(dx + (t0 + q) * row_bytes + lane_off, dx_out[q]);
             }
         }
         __syncthreads();
@@ -455,9 +474,9 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
 // every run). A partial is [slices][W+1][64 lanes][4] fp32 = nb blocks of 256 floats.
 //  stage A: block b of the partials summed over a chunk of kChunk groups, in group order, in fp64
 //           (one thread per float, coalesced loads of all groups in flight);
-//  stage B: the taps gradient sums its element's chunk sums in chunk order; the gamma gradient,
-//           a sum over heads as well, takes one wave per output: lane l adds the (head, chunk)
-//           pairs l, l+64, ... in order and a butterfly adds the 64 lane sums.
+//  stage B (one launch): the taps gradient sums its element's chunk sums in chunk order; the
+//           gamma gradient, a sum over heads as well, takes one wave per output: lane l adds the
+//           (head, chunk) pairs l, l+64, ... in order and a butterfly adds the 64 lane sums.
 constexpr int kChunk = 64;
 
 template <int W>
@@ -480,31 +499,31 @@ __device__ inline int64_t partial_index(const BwdArgs& a, int t, int k, int64_t 
     return ((gl / 64) * (W + 1) + k) * 256 + (gl % 64) * 4 + ch % 4;
 }
 
+// Stage B. Blocks [0, taps_blocks) give the taps gradient, one thread per element; the rest give
+// the gamma gradient, one wave per element.
 template <int W>
-__global__ void __launch_bounds__(256) backward_taps_kernel(BwdArgs a, int D) {
-    const int64_t HD = (int64_t)a.heads * D;
-    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (id >= 2 * W * HD) return;
-    const int t = (int)(id / (W * HD));
-    const int64_t r = id - (int64_t)t * W * HD;
-    const int k = (int)(r / HD);
-    const int64_t ch = r - (int64_t)k * HD;
+__global__ void __launch_bounds__(256) backward_final_kernel(BwdArgs a, int D, int taps_blocks) {
     const int64_t per_chunk = (int64_t)a.slices * (W + 1) * 256;
-    const double* src = a.chunk + partial_index<W>(a, t, k, ch);
-    double acc = 0.0;
+    if ((int)blockIdx.x < taps_blocks) {
+        const int64_t HD = (int64_t)a.heads * D;
+        const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+        if (id >= 2 * W * HD) return;
+        const int t = (int)(id / (W * HD));
+        const int64_t r = id - (int64_t)t * W * HD;
+        const int k = (int)(r / HD);
+        const int64_t ch = r - (int64_t)k * HD;
+        const double* src = a.chunk + partial_index<W>(a, t, k, ch);
+        double acc = 0.0;
 #pragma unroll 8
-    for (int c = 0; c < a.chunks; ++c) acc += src[c * per_chunk];
-    pick(a.dtaps, t)[r] = (float)acc;
-}
-
-template <int W>
-__global__ void __launch_bounds__(256) backward_gamma_kernel(BwdArgs a, int D) {
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+        for (int c = 0; c < a.chunks; ++c) acc += src[c * per_chunk];
+        pick(a.dtaps, t)[r] = (float)acc;
+        return;
+    }
+    const int64_t wave = (int64_t)(blockIdx.x - taps_blocks) * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (wave >= 2 * D) return;  // whole waves leave together
     const int t = (int)(wave / D);
     const int d = (int)(wave - (int64_t)t * D);
-    const int64_t per_chunk = (int64_t)a.slices * (W + 1) * 256;
     const int64_t pairs = (int64_t)a.heads * a.chunks;
     double acc = 0.0;
     for (int64_t i = lane; i < pairs; i += 64) {
@@ -528,11 +547,10 @@ const BwdFn kBackward[2][3][8] = {
     {SC_BROW(BF16, 64), SC_BROW(BF16, 128), SC_BROW(BF16, 256)},
 };
 using ChunkFn = void (*)(BwdArgs);
-using FinalFn = void (*)(BwdArgs, int);
+using FinalFn = void (*)(BwdArgs, int, int);
 #define SC_PER_W(K) {K<1>, K<2>, K<3>, K<4>, K<5>, K<6>, K<7>, K<8>}
 const ChunkFn kChunkSum[8] = SC_PER_W(backward_chunk_kernel);
-const FinalFn kTaps[8] = SC_PER_W(backward_taps_kernel);
-const FinalFn kGamma[8] = SC_PER_W(backward_gamma_kernel);
+const FinalFn kFinal[8] = SC_PER_W(backward_final_kernel);
 
 int d_index(int D) { return D == 64 ? 0 : (D == 128 ? 1 : 2); }
 
@@ -544,10 +562,13 @@ BwdShape backward_shape(int64_t total_tokens, int32_t num_seqs, int32_t num_head
     sh.lanes_per_tensor = (int64_t)num_heads * head_dim / 4;
     sh.slices = (2 * sh.lanes_per_tensor + 63) / 64;
     const int bt = dtype == 1 ? (width <= 5 ? bwd_span<BF16, 1>() : bwd_span<BF16, 8>())
-                              : (width <= 3 ? bwd_span<F32, 1>() : bwd_span<F32, 8>());
+                              : (width <= 1 ? bwd_span<F32, 1>() : bwd_span<F32, 8>());
     const int64_t bb = (int64_t)kBwdWaves * bt;
     sh.tiles = total_tokens / bb + num_seqs;
-    sh.groups = (sh.tiles + kTilesPerGroup - 1) / kTilesPerGroup;
+    int64_t per = sh.tiles * sh.slices / kFillBlocks;
+    per = per < 1 ? 1 : (per > kMaxTilesPerGroup ? kMaxTilesPerGroup : per);
+    sh.tiles_per_group = per;
+    sh.groups = (sh.tiles + per - 1) / per;
     sh.chunks = (sh.groups + kChunk - 1) / kChunk;
     const int64_t nb = sh.slices * (width + 1);  // 256-float blocks per partial
     sh.partial_bytes = (size_t)sh.groups * nb * 256 * 4;
@@ -565,10 +586,10 @@ hipError_t launch_backward(BwdArgs a, int dtype, int head_dim, int width, hipStr
                            0, stream, a);
     }
     const int64_t taps = 2 * (int64_t)width * a.heads * head_dim;
-    hipLaunchKernelGGL(kTaps[width - 1], dim3((unsigned)((taps + 255) / 256)), dim3(256), 0,
-                       stream, a, head_dim);
-    hipLaunchKernelGGL(kGamma[width - 1], dim3((unsigned)((2 * head_dim + 3) / 4)), dim3(256), 0,
-                       stream, a, head_dim);
+    const int taps_blocks = (int)((taps + 255) / 256);
+    const int gamma_blocks = (2 * head_dim + 3) / 4;
+    hipLaunchKernelGGL(kFinal[width - 1], dim3((unsigned)(taps_blocks + gamma_blocks)), dim3(256),
+                       0, stream, a, head_dim, taps_blocks);
     return hipGetLastError();
 }
 

@@ -65,6 +65,7 @@ struct BwdArgs {
     int32_t tiles;             // logical tiles (upper bound, as in prefill)
     int32_t groups;            // workgroups per column slice (each walks a few tiles)
     int32_t chunks;            // groups are first summed in chunks (of 64)
+    int32_t tiles_per_group;   // consecutive tiles one workgroup walks (1..4)
     float eps;
 };
 
@@ -74,6 +75,7 @@ struct BwdShape {
     int64_t slices;
     int64_t tiles;
     int64_t groups;
+    int64_t tiles_per_group;
     int64_t chunks;
     size_t partial_bytes;      // the fp32 partials; the fp64 chunk sums follow them
     size_t workspace_bytes;
