@@ -53,7 +53,7 @@ constexpr int64_t kFillBlocks = 2048;
 #define SC_BWD_BT_BF16 16       // bf16, W <= 5
 #endif
 #ifndef SC_BWD_BT_BF16_WIDE
-#define SC_BWD_BT_BF16_WIDE 8   // bf16, W > 5
+#define SC_BWD_BT_BF16_WIDE 10  // bf16, W > 5
 #endif
 #ifndef SC_BWD_BT_F32
 #define SC_BWD_BT_F32 16        // fp32, W == 1
@@ -192,6 +192,8 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
     static_assert(BT >= R, "a wave's span must cover the window");
     // dc rows that wave w + 1 hands back to wave w (first R of its span), reused afterwards for
     // the workgroup's sum of the parameter-gradient partials.
+    constexpr bool kPrefetchNext = R <= 3;
+
     constexpr int kHand = NW * RR;
     constexpr int kRed = (NW - 1) * (W + 1);
     __shared__ float4 lds[(kHand > kRed ? kHand : kRed) * 64];
@@ -274,6 +276,7 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
         float win[W][4];
         float dcr[W][4];  // ring: slot (i % W) holds dc of span token i
         Raw gsr[RR];
+        Raw xn[RR], gn[RR];  // the last wave's rows after its span (phase 2)
         if (n > 0) {
             // ---- phase 1: one burst of loads, then the span's tokens ----
             const char* hsrc = !first_span ? x + (t0 - R) * xs
@@ -287,6 +290,17 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
             if (has_tail) {
 #pragma unroll
                 for (int m = 0; m < R; ++m) gsr[m] = Q::load(gs_seq + m * row_bytes + lane_off);
+            }
+            // the tile's last wave also fetches the R rows after its span now, for phase 2
+            // (narrow windows only: wide ones have no registers to spare)
+            if (kPrefetchNext && w == NW - 1 && next_n > 0) {
+                const int lastn = next_n - 1;
+#pragma unroll
+                for (int k = 0; k < R; ++k) {
+                    const int r = k < lastn ? k : lastn;
+                    xn[k] = Q::load(x + (t0 + BT + r) * xs + lane_off);
+                    gn[k] = Q::load(dy + (t0 + BT + r) * row_bytes + lane_off);
+                }
             }
 #pragma unroll
             for (int k = 0; k < R; ++k) halo[k] = Q::load(hsrc + k * hstride + lane_off);
@@ -312,7 +326,6 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
             // the compiler waits for each token's rows alone and the first tokens are computed
             // while later rows arrive; a store among them would make it wait for everything.
             Raw dx_out[BT - R > 0 ? BT - R : 1];
-            Raw ds_out[RR];
 #pragma unroll
             for (int i = 0; i < BT; ++i) {
                 float dci[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -333,26 +346,6 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
                 for (int v = 0; v < 4; ++v) dcr[i % W][v] = dci[v];
                 if (i < R)
                     lds[(w * RR + i) * 64 + wl] = make_float4(dci[0], dci[1], dci[2], dci[3]);
-                // the initial window's gradient, once the first R dc are known
-                if (R > 0 && i == R - 1 && first_span && dstate != nullptr) {
-#pragma unroll
-                    for (int m = 0; m < R; ++m) {
-                        float de[4];
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) de[v] = 0.0f;
-#pragma unroll
-                        for (int k = 0; k <= m; ++k)
-#pragma unroll
-                            for (int v = 0; v < 4; ++v)
-                                de[v] = __builtin_fmaf(tap[k][v], dcr[(m - k) % W][v], de[v]);
-                        if (has_tail) add_state_loss<E, R>(gsr, (int64_t)m - L, de);
-                        if (!from_state) {
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) de[v] = 0.0f;
-                        }
-                        ds_out[m] = Q::narrow(de);
-                    }
-                }
                 // rows whose dc window lies inside the span: q = i - R
                 if (i >= R && i - R < n) {
                     const int q = i - R;
@@ -362,15 +355,37 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
                     dx_out[q] = Q::narrow(de);
                 }
             }
-            if (R > 0 && first_span && dstate != nullptr && active) {
-#pragma unroll
-                for (int m = 0; m < R; ++m)
-                    Q::store(dstate + ((int64_t)s * R + m) * row_bytes + lane_off, ds_out[m]);
-            }
             if (active) {
 #pragma unroll
                 for (int q = 0; q < BT - R; ++q)
                     if (q < n) Q::store(dx + (t0 + q) * row_bytes + lane_off, dx_out[q]);
+            }
+            // The initial window's gradient (first span): de[m] = sum_{k<=m} taps[k] dc[m-k],
+            // from the span's first R dc, which this wave also left in LDS for its neighbour.
+            if (R > 0 && first_span && dstate != nullptr) {
+                float d0c[RR][4];
+#pragma unroll
+                for (int k = 0; k < R; ++k) {
+                    const float4 f = lds[(w * RR + k) * 64 + wl];
+                    d0c[k][0] = f.x; d0c[k][1] = f.y; d0c[k][2] = f.z; d0c[k][3] = f.w;
+                }
+#pragma unroll
+                for (int m = 0; m < R; ++m) {
+                    float de[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int k = 0; k <= m; ++k)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            de[v] = __builtin_fmaf(tap[k][v], d0c[m - k][v], de[v]);
+                    if (has_tail) add_state_loss<E, R>(gsr, (int64_t)m - L, de);
+                    if (!from_state) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) de[v] = 0.0f;
+                    }
+                    if (active)
+                        Q::store(dstate + ((int64_t)s * R + m) * row_bytes + lane_off,
+                                 Q::narrow(de));
+                }
             }
         }
         __syncthreads();
@@ -391,15 +406,15 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
                 } else {
                     // the tile's last wave: recompute the next tile's first next_n tokens (the
                     // input window continues from the span's last rows)
-                    Raw xn[RR], gn[RR];
-                    const int lastn = next_n - 1;
+                    if (!kPrefetchNext) {
+                        const int lastn = next_n - 1;
 #pragma unroll
-                    for (int k = 0; k < R; ++k) {
-                        const int r = k < lastn ? k : lastn;
-                        xn[k] = Q::load(x + (t0 + BT + r) * xs + lane_off);
-                        gn[k] = Q::load(dy + (t0 + BT + r) * row_bytes + lane_off);
+                        for (int k = 0; k < R; ++k) {
+                            const int r = k < lastn ? k : lastn;
+                            xn[k] = Q::load(x + (t0 + BT + r) * xs + lane_off);
+                            gn[k] = Q::load(dy + (t0 + BT + r) * row_bytes + lane_off);
+                        }
                     }
-                    wait_vmem();
 #pragma unroll
                     for (int k = 0; k < R; ++k) {
                         const int i = BT + k;

@@ -218,8 +218,8 @@ def test_backward_workspace_size(lib):
     # fp32 partial of (W + 1) * 64 lanes * 4 channels per slice and group, then fp64 sums of
     # chunks of 64 groups (5 chunks)
     assert size(17060, 8, 8, 128, 4, 1) == 274 * 8 * 5 * 256 * 4 + 5 * 8 * 5 * 256 * 8
-    # the long prefill (W=8 -> 8-token spans): 131072 // 32 + 1 = 4097 tiles, 4 per group
-    assert size(131072, 1, 8, 128, 8, 1) == 1025 * 8 * 9 * 256 * 4 + 17 * 8 * 9 * 256 * 8
+    # the long prefill (W=8 -> 10-token spans): 131072 // 40 + 1 = 3277 tiles, 4 per group
+    assert size(131072, 1, 8, 128, 8, 1) == 820 * 8 * 9 * 256 * 4 + 13 * 8 * 9 * 256 * 8
     assert size(0, 0, 8, 128, 4, 1) == 0
     assert size(10, 2, 8, 96, 4, 1) == 2 ** 64 - 1  # unsupported head_dim -> SIZE_MAX
     assert "head_dim" in lib.shortconv_last_error().decode()
