@@ -501,14 +501,17 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(StepArgs a) {
 // which it only reads; the state after every token goes to a snapshot buffer instead, so that the
 // state of any accepted prefix can be installed afterwards (commit_kernel).
 // ------------------------------------------------------------------------------------------------
-constexpr int kVerifyChunk = 16;  // tokens whose rows are loaded together per pass
+// Tokens whose rows are loaded together per pass: about 16, a multiple of the window width.
+template <int W>
+constexpr int verify_chunk() { return W * (16 / W); }
 
 template <class E, int D, int W>
 __global__ void __launch_bounds__(kBlock) verify_kernel(StepArgs a, VerifyArgs va) {
     constexpr int VEC = E::VEC;
     constexpr int LPH = D / VEC;
     constexpr int R = W - 1;
-    constexpr int K = kVerifyChunk;
+    constexpr int K = verify_chunk<W>();
+    static_assert(K <= 64, "a wave loads one slot per lane");
     const int s = blockIdx.x;
     const int lane = blockIdx.y * kBlock + threadIdx.x;
     if (lane >= 2 * a.lanes_per_tensor) return;
@@ -534,48 +537,51 @@ __global__ void __launch_bounds__(kBlock) verify_kernel(StepArgs a, VerifyArgs v
 
     LaneParams<E, W> p;
     load_params<E, W>(pick(a.taps, tensor), pick(a.gamma, tensor), a.heads, D, h, d0, p);
-    // Rolling window of raw rows (for bit-exact snapshots) and its widened copy.
-    uint4 rw[R > 0 ? R : 1];
+    // The window as two rings of W rows (raw, for bit-exact snapshots, and widened): token t's
+    // row goes to slot (t + R) % W. A chunk is a multiple of W tokens, so every slot index is a
+    // compile-time constant and advancing the window moves no registers. The stored state comes
+    // in from a valid stand-in (the taps) when the sequence has no state slot, then is cleared.
+    uint4 rr[W];
     float win[W][VEC];
+    const char* src = slot_ok ? state + (int64_t)idx * R * row_bytes
+                              : reinterpret_cast<const char*>(pick(a.taps, tensor));
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
-        rw[k] = slot_ok ? ldrow(state + ((int64_t)idx * R + k) * row_bytes, lane_off)
-                        : make_uint4(0, 0, 0, 0);
-        E::widen(rw[k], win[k]);
-    }
+    for (int k = 0; k < R; ++k) rr[k] = ldrow(src + k * row_bytes, lane_off);
     const float inv_d = 1.0f / (float)D;
     char* snap_seq = snap + (int64_t)s * va.max_tokens * R * row_bytes;
+    const int wl = threadIdx.x & 63;
 
     for (int64_t c0 = 0; c0 < L; c0 += K) {
+        // the chunk's rows (past the run's end the last row again, unused) and, in lane i, the
+        // cache slot of its token i
+        const int64_t last = (L - c0 < K ? L - c0 : K) - 1;
         uint4 raw[K];
-        int64_t slot[K];
 #pragma unroll
-        for (int i = 0; i < K; ++i) {
-            if (c0 + i < L) {
-                raw[i] = ldrow(x + (start + c0 + i) * stride_bytes, lane_off);
-                slot[i] = a.slot[start + c0 + i];
+        for (int i = 0; i < K; ++i)
+            raw[i] = ldrow(x + (start + c0 + (i < last ? i : last)) * stride_bytes, lane_off);
+        const int64_t lane_slot = a.slot[start + c0 + (wl < last ? wl : last)];
+        if (c0 == 0) {  // the initial rows, the oldest loads, while this chunk's are in flight
+#pragma unroll
+            for (int k = 0; k < R; ++k) {
+                if (!slot_ok) rr[k] = make_uint4(0, 0, 0, 0);
+                E::widen(rr[k], win[k]);
             }
         }
+        wait_vmem();  // the stores below then never wait for anything
 #pragma unroll
         for (int i = 0; i < K; ++i) {
             if (c0 + i < L) {
-                E::widen(raw[i], win[R]);
+                rr[(i + R) % W] = raw[i];
+                E::widen(raw[i], win[(i + R) % W]);
                 float o[VEC];
-                fused_row<E, W, LPH>(win, 0, p, a.eps, inv_d, o);
-                sink.put(slot[i], true, o);
+                fused_row<E, W, LPH>(win, i % W, p, a.eps, inv_d, o);
+                sink.put(lane_value(lane_slot, i), true, o);
+                if (R > 0 && snap != nullptr && c0 + i < va.max_tokens) {
+                    // the state after this token: its row and the R - 1 before it, oldest first
+                    char* dst = snap_seq + (c0 + i) * R * row_bytes;
 #pragma unroll
-                for (int k = 0; k < R; ++k)
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v) win[k][v] = win[k + 1][v];
-                if (R > 0) {
-#pragma unroll
-                    for (int k = 0; k + 1 < R; ++k) rw[k] = rw[k + 1];
-                    rw[R - 1] = raw[i];
-                    if (snap != nullptr && c0 + i < va.max_tokens) {
-                        char* dst = snap_seq + (c0 + i) * R * row_bytes;
-#pragma unroll
-                        for (int k = 0; k < R; ++k) strow(dst + k * row_bytes, lane_off, rw[k]);
-                    }
+                    for (int k = 0; k < R; ++k)
+                        strow(dst + k * row_bytes, lane_off, rr[(i + 1 + k) % W]);
                 }
             }
         }
