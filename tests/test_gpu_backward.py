@@ -142,6 +142,7 @@ SHAPES = [
     ("f32", 4, 128, 8, [30, 6, 71], [1, 0, 1]),
     ("f32", 2, 256, 3, [2, 50, 0, 13], [1, 1, 1, 0]),
     ("bf16", 16, 128, 6, [200, 3], [1, 1]),
+    ("bf16", 40, 256, 4, [30, 2, 0, 9], [1, 0, 1, 1]),  # 80 column slices of K|V
 ]
 
 

@@ -127,7 +127,7 @@ def _written_slots(w):
     return s[(s >= 0) & (s < w.num_slots)]
 
 
-@pytest.mark.parametrize("H,D,W", [(2, 64, 4), (3, 128, 8), (1, 256, 2)])
+@pytest.mark.parametrize("H,D,W", [(2, 64, 4), (3, 128, 8), (1, 256, 2), (12, 256, 3)])
 def test_fused_mx_equals_quantized_fp32_output(H, D, W):
     spec = workloads.Spec(dtype="f32", H=H, D=D, W=W, seed=40 + W, prefill_lens=[37, 0, 5, 100],
                           has_init=[1, 0, 1, 0], decode_ctx=[3, 50], pad_slot_every=13,
