@@ -177,18 +177,22 @@ struct PlainSink {
     }
 };
 
-// OCP FP8 E4M3 codes of four finite values, byte b = code of v[b]: nearest value, ties to even,
-// saturating at +-448. gfx950's packed conversion rounds to nearest even into the OCP format but
-// does not saturate, so the values are clamped to the largest finite code first.
-__device__ inline uint32_t e4m3x4(float v0, float v1, float v2, float v3) {
-    constexpr float kMax = 448.0f;
-    v0 = __builtin_amdgcn_fmed3f(v0, -kMax, kMax);
-    v1 = __builtin_amdgcn_fmed3f(v1, -kMax, kMax);
-    v2 = __builtin_amdgcn_fmed3f(v2, -kMax, kMax);
-    v3 = __builtin_amdgcn_fmed3f(v3, -kMax, kMax);
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
-    return (uint32_t)w;
+// OCP FP8 E4M3 codes of v[b] * 2^-e for four finite values (byte b): nearest value, ties to even,
+// saturating at +-448. gfx950's scaled conversion (v_cvt_scalef32_pk_fp8_f32) divides by its
+// scale operand, here 2^e, exactly and rounds to nearest even into the OCP format, but does not
+// saturate; clamping v to +-448 * 2^e first is the same as clamping v * 2^-e to +-448, scaling by
+// a power of two being exact.
+typedef short sc_i16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t e4m3x4_scaled(float v0, float v1, float v2, float v3, float scale,
+                                         float lim) {
+    v0 = __builtin_amdgcn_fmed3f(v0, -lim, lim);
+    v1 = __builtin_amdgcn_fmed3f(v1, -lim, lim);
+    v2 = __builtin_amdgcn_fmed3f(v2, -lim, lim);
+    v3 = __builtin_amdgcn_fmed3f(v3, -lim, lim);
+    sc_i16x2 w = {0, 0};
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, v0, v1, scale, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, v2, v3, scale, true);
+    return __builtin_bit_cast(uint32_t, w);
 }
 
 // MXFP8 rows: 32-element blocks along head_dim share one E8M0 scale 2^e with
@@ -229,11 +233,12 @@ struct MxSink {
         int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 1 - 8 : -127;
         e = e < -127 ? -127 : (e > 127 ? 127 : e);
         r.e = e;
+        const float scale = __builtin_ldexpf(1.0f, e);
+        const float lim = __builtin_ldexpf(448.0f, e);  // +inf at e = 127: nothing saturates there
 #pragma unroll
         for (int q = 0; q < VEC / 4; ++q)
-            r.packed[q] = e4m3x4(__builtin_ldexpf(o[4 * q], -e), __builtin_ldexpf(o[4 * q + 1], -e),
-                                 __builtin_ldexpf(o[4 * q + 2], -e),
-                                 __builtin_ldexpf(o[4 * q + 3], -e));
+            r.packed[q] = e4m3x4_scaled(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3], scale,
+                                        lim);
         return r;
     }
     __device__ void write(int64_t slot, bool active, const Enc& enc) const {
