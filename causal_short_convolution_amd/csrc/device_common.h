@@ -68,6 +68,10 @@ __device__ inline uint4 ldrow(const char* base, uint32_t lane_off) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + lane_off));
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+// The same load without the streaming hint: the line stays in L2 for a later reader.
+__device__ inline uint4 ldrow_keep(const char* base, uint32_t lane_off) {
+    return *reinterpret_cast<const uint4*>(base + lane_off);
+}
 __device__ inline void strow(char* base, uint32_t lane_off, const uint4& v) {
     const u32x4 w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(base + lane_off));
