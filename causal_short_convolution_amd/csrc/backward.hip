@@ -79,6 +79,9 @@ struct Quad<F32> {
         const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
         return make_uint4(v.x, v.y, v.z, v.w);
     }
+    __device__ static Raw load_keep(const char* p) {  // without the streaming hint
+        return *reinterpret_cast<const uint4*>(p);
+    }
     __device__ static void store(char* p, const Raw& r) {
         const u32x4 v = {r.x, r.y, r.z, r.w};
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
@@ -102,6 +105,9 @@ struct Quad<BF16> {
     __device__ static Raw load(const char* p) {
         const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
         return make_uint2(v.x, v.y);
+    }
+    __device__ static Raw load_keep(const char* p) {  // without the streaming hint
+        return *reinterpret_cast<const uint2*>(p);
     }
     __device__ static void store(char* p, const Raw& r) {
         const u32x2 v = {r.x, r.y};
@@ -302,13 +308,16 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
                     gn[k] = Q::load(dy + (t0 + BT + r) * row_bytes + lane_off);
                 }
             }
+            // The halo and the span's last R input rows are loaded without the streaming hint,
+            // the other rows with it, the mix that measured fastest (as in the forward).
 #pragma unroll
-            for (int k = 0; k < R; ++k) halo[k] = Q::load(hsrc + k * hstride + lane_off);
+            for (int k = 0; k < R; ++k) halo[k] = Q::load_keep(hsrc + k * hstride + lane_off);
             const int last = n - 1;
 #pragma unroll
             for (int i = 0; i < BT; ++i) {
                 const int r = i < last ? i : last;
-                xr[i] = Q::load(x + (t0 + r) * xs + lane_off);
+                xr[i] = i >= BT - R ? Q::load_keep(x + (t0 + r) * xs + lane_off)
+                                    : Q::load(x + (t0 + r) * xs + lane_off);
                 gr[i] = Q::load(dy + (t0 + r) * row_bytes + lane_off);
             }
             if (first_span && !from_state) {

@@ -352,15 +352,16 @@ __global__ void __launch_bounds__(kBlock, (span_min_waves<W, MX>())) prefill_ker
                                             : reinterpret_cast<const char*>(pick(a.taps, tensor));
             const int64_t hstride = j > 0 ? stride_bytes : row_bytes;
 #pragma unroll
-            for (int k = 0; k < R; ++k) halo[k] = ldrow(hsrc + k * hstride, lane_off);
+            for (int k = 0; k < R; ++k) halo[k] = ldrow_keep(hsrc + k * hstride, lane_off);
         }
         // Past a short span's end the last row is read again (and not used). Lane l < BT loads
         // token l's cache slot (one vector load instead of BT scalar ones, which the compiler
         // would issue only after the rows arrive).
         const int last = n - 1;
-        // The R rows at the end of the span are loaded without the streaming hint, the others
-        // with it: measured on MI355X, this mix is faster than either all streaming (varlen bf16
-        // prefill 30.3 -> 28.5 us) or none; why it beats all-streaming is not established.
+        // The R rows at the end of the span (and the first wave's halo rows, above) are loaded
+        // without the streaming hint, the others with it: measured on MI355X, this mix is faster
+        // than all streaming (varlen bf16 prefill 30.3 -> 28.1 us) or none, with unchanged HBM
+        // reads in the counters; why it is faster is not established.
 #pragma unroll
         for (int i = BT - R; i < BT; ++i)
             raw[i] = ldrow_keep(xb + (i < last ? i : last) * stride_bytes, lane_off);
