@@ -687,6 +687,31 @@ def pin_backward_invariants():
         assert abs(dg - gy) <= 1e-12 * float(np.abs(g * y).sum()), f"gamma linearity (W={W})"
 
 
+def pin_backward_locality():
+    """The input gradient of token t depends on rows t-R .. t+R only: the full sequence's dx[t]
+    equals the first row's gradient of the short sequence t .. t+R (cut at the sequence's end)
+    that resumes from rows t-R .. t-1 as its stored state."""
+    for W in (4, 2, 7):
+        R = W - 1
+        w, st, g, _ = _bwd_case(W=W, D=64, lens=(30, 5), hin=(1, 1), seed=41)
+        full = oracle.backward_one(st.k, st.cu_seqlens, w.k_taps, w.k_gamma, w.eps, w.k_state,
+                                   st.state_idx, st.has_init, g)
+        x64 = st.k
+        for s in range(2):
+            a, b = int(st.cu_seqlens[s]), int(st.cu_seqlens[s + 1])
+            z = w.k_state[st.state_idx[s]]
+            e = np.concatenate([z, x64[a:b]], axis=0)  # stored rows, state first
+            for p in range(b - a):
+                rows = e[p + R: min(p + R + 1 + R, R + b - a)]
+                st_rows = e[p:p + R][None]
+                n = rows.shape[0]
+                part = oracle.backward_one(np.ascontiguousarray(rows), np.array([0, n]), w.k_taps,
+                                           w.k_gamma, w.eps, np.ascontiguousarray(st_rows),
+                                           np.array([0]), np.array([1]), g[a + p:a + p + n])
+                assert np.allclose(part.dx[0], full.dx[a + p], rtol=1e-12, atol=1e-12), \
+                    f"locality of dx (W={W}, seq {s}, token {p})"
+
+
 ALL_PINS = [
     pin_exact_rational,
     pin_torch_conv1d_rmsnorm,
@@ -708,4 +733,5 @@ ALL_PINS = [
     pin_backward_finite_differences,
     pin_backward_torch_autograd,
     pin_backward_invariants,
+    pin_backward_locality,
 ]
