@@ -183,7 +183,8 @@ int shortconv_mxfp8_quantize(const void* x, int64_t tok_stride, int64_t rows, in
  *                   rows, oldest first), written for i < min(L_s, max_tokens); other entries are
  *                   not written. May be NULL when width == 1.
  *  max_tokens       >= 1, the snapshot capacity per sequence (the longest candidate run).
- * Sequences are processed 16 tokens per pass; candidate runs are meant to be short.
+ * Sequences are processed in passes of about 16 tokens (a multiple of the width); candidate runs
+ * are meant to be short.
  */
 int shortconv_kv_verify(const void* k, const void* v, int64_t k_tok_stride, int64_t v_tok_stride,
                         const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
