@@ -187,3 +187,40 @@ def test_mx_rejects_missing_scales():
         shortconv_kv_prefill_mxfp8(d["k"], d["v"], d["cu"], dw.k_taps, dw.v_taps, dw.k_gamma,
                                    dw.v_gamma, w.eps, dw.k_state, dw.v_state, d["sidx"],
                                    d["hinit"], d["slot"], codes, codes.clone(), None, None)
+
+
+def test_fused_mx_bf16_equals_quantized_plain_rows_but_double_rounding():
+    """bf16 I/O: the plain and the MXFP8 prefill compute the same fp32 rows (same lane layout,
+    same arithmetic); the plain one rounds them to bf16. Quantizing those bf16 rows with the
+    oracle gives the MXFP8 kernel's codes and scales exactly, except where rounding to bf16 first
+    can flip a decision: a scaled element exactly on an E4M3 midpoint (one step apart), or a
+    block whose bf16 maximum is exactly a power of two (its scale one below)."""
+    spec = workloads.Spec(dtype="bf16", H=8, D=128, W=4, seed=61, prefill_lens=[700, 33, 1500],
+                          has_init=[1, 0, 1], decode_ctx=[12, 90], outlier_p=0.01)
+    w = workloads.build(spec)
+    plain, mx = _fused_pair(w)
+    rows = _written_slots(w)
+    mids = oracle.e4m3_decode(np.arange(0, 0x7E))
+    mids = (mids + oracle.e4m3_decode(np.arange(1, 0x7F))) / 2.0
+    flips = 0
+    for cache, codes_d, scales_d in ((plain.k_cache, mx.k_codes, mx.k_scales),
+                                     (plain.v_cache, mx.v_codes, mx.v_scales)):
+        yb = oracle.widen(to_host(cache, "bf16")[rows])
+        ec, es = oracle.mxfp8_quantize(yb)
+        gc, gs = codes_d.cpu().numpy()[rows], scales_d.cpu().numpy()[rows]
+        blocks = np.abs(yb).reshape(*yb.shape[:-1], -1, 32).max(-1)
+        pow2 = (blocks > 0) & (np.frexp(blocks)[0] == 0.5)
+        bad_scale = gs != es
+        assert (pow2 | ~bad_scale).all(), "a scale differs off a power-of-two block maximum"
+        assert ((es.astype(int) - gs.astype(int))[bad_scale] == 1).all()
+        same = np.repeat(gs == es, 32, axis=-1)
+        e = np.repeat(es.astype(np.int64) - 127, 32, axis=-1)
+        scaled = np.abs(yb) * np.exp2(-e.astype(np.float64))
+        tie = np.isin(scaled, mids)
+        diff = (gc != ec) & same
+        assert (tie | ~diff).all(), "a code differs off an E4M3 midpoint"
+        step = np.abs(oracle.e4m3_decode(gc) - oracle.e4m3_decode(ec))
+        gap = np.maximum(np.abs(oracle.e4m3_decode(ec)) * 2.0 ** -3, 2.0 ** -9)
+        assert (step[diff] <= gap[diff] * (1 + 1e-12)).all(), "a flipped code is more than a step"
+        flips += int(diff.sum()) + int(bad_scale.sum())
+    print(f"double-rounding flips: {flips}")
