@@ -124,7 +124,9 @@ constexpr int kRowMirror = 0x140;     // lane i <-> 15-i within each row
 // each lane adds its value and its partner's, the partner adds the same two values in the other
 // order, so all lanes of the group end with the same bits. Within a 16-lane row the partners come
 // from DPP moves; the quad steps make the 4 lanes of a quad equal, so the mirror moves pair each
-// lane with a lane of the neighbouring quad (half row) or half row (row).
+// lane with a lane of the neighbouring quad (half row) or half row (row). Across rows, gfx950's
+// permlane swaps give every lane its own value and its partner's (lane ^ 16, lane ^ 32) in one
+// VALU instruction, as two outputs whose sum is own + partner in every lane.
 template <int LPH>
 __device__ inline float head_sum(float v) {
     static_assert(LPH == 8 || LPH == 16 || LPH == 32 || LPH == 64, "lanes per head");
@@ -132,8 +134,16 @@ __device__ inline float head_sum(float v) {
     v += dpp<kQuadXor2>(v);
     v += dpp<kRowHalfMirror>(v);
     if (LPH >= 16) v += dpp<kRowMirror>(v);
-    if (LPH >= 32) v += __shfl_xor(v, 16, 64);
-    if (LPH >= 64) v += __shfl_xor(v, 32, 64);
+    if (LPH >= 32) {
+        const uint32_t u = __float_as_uint(v);
+        const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+    if (LPH >= 64) {
+        const uint32_t u = __float_as_uint(v);
+        const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
     return v;
 }
 
