@@ -106,6 +106,21 @@ def verify_bytes(w, accepted, max_tokens):
     return verify, commit
 
 
+def input_digest(w):
+    """sha256 (first 16 hex digits) of every input array of workload w, in a fixed order: the
+    bench's numbers are tied to exactly these inputs."""
+    import numpy as np
+    h = hashlib.sha256()
+    for a in (w.k_taps, w.v_taps, w.k_gamma, w.v_gamma, w.k_state, w.v_state):
+        if a is not None:
+            h.update(np.ascontiguousarray(a).tobytes())
+    for st in w.steps:
+        for a in (st.k, st.v, st.slot_mapping, st.state_idx, st.cu_seqlens, st.has_init):
+            if a is not None:
+                h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()[:16]
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -600,7 +615,8 @@ def main():
                    "tokens_per_step": w.tokens, "launches_per_step": len(w.steps),
                    "seqs": sum(x.num_seqs for x in w.steps), "heads": w.H,
                    "head_dim": w.D, "width": w.W, "io": w.dtype, "block_size": w.block_size,
-                   "replicas": main_m["replicas"], "parallelism": "single GPU"},
+                   "replicas": main_m["replicas"], "input_sha256": input_digest(w),
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": main_m["achieved_GBps"], "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": main_m["achieved_GBps"] / HBM_PEAK_GBPS,
                      "traffic": traffic,
