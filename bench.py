@@ -39,7 +39,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
 MALL_BYTES = 256 << 20          # MI355X Infinity Cache
 KERNEL_SRC = [os.path.join(ROOT, "causal_short_convolution_amd", "csrc", f)
               for f in ("kernels.hip", "device_common.h")]
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_varlen_bf16_traffic.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "varlen_bf16_all_kernels_traffic.md")
 WORKLOADS = {"tiny_ref": 1, "varlen_prefill": 2, "decode": 3, "long_prefill": 4, "mixed": 5}
 COPY_BYTES = 512 << 20          # calibration copy: 512 MiB read + 512 MiB written
 KERNELS = ("prefill_kernel", "decode_kernel", "verify_kernel", "commit_kernel",

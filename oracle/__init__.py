@@ -3,9 +3,11 @@
 Only the test suite, the smoke check and the bench's CPU-baseline leg may import this package.
 The HIP library never does, and this package imports nothing from it.
 
-The arithmetic lives in ``shortconv_oracle.c`` (fp64, one plain loop nest per definition step;
-its header states the definition and the readings of the pages it follows). This module only
-marshals numpy arrays into it and applies the two scatters the step ends with:
+The step's arithmetic and its backward live in ``shortconv_oracle.c`` (fp64, one plain loop nest
+per definition step; its header states the definition and the readings of the pages it follows).
+This module marshals numpy arrays into it, writes out in numpy the parts that are bit copies or
+encodings (the speculative-verification snapshots and commit, the MXFP8 encoding), holds the
+acceptance metric, and applies the two scatters the step ends with:
 
 * the cache write: row ``y[t]`` goes to ``cache[slot_mapping[t]]`` when ``0 <= slot < num_slots``
   (aib.vote English news item on SGLang/Miles day-0 Inkling support, paragraph 2: the fused
@@ -229,80 +231,6 @@ def fused_decode(k_new, v_new, k_taps, v_taps, k_gamma, v_gamma, eps, k_state, v
 # English news item on SGLang/Miles Inkling support, paragraph 3; data-sketchers.com SGLang
 # cookbook for Inkling-Small, section 2 (MTP) and section 3.7 (DSpark)).
 # ---------------------------------------------------------------------------------------------
-@dataclass
-class Grads:
-    """Gradients of one tensor's step (all fp64): dx [T,H,D], dtaps [W,H,D], dgamma [D], and
-    dstate [N,W-1,H,D] (None when W == 1), the gradient of each sequence's initial window rows
-    (zero for a sequence that started from zeros)."""
-    dx: np.ndarray
-    dtaps: np.ndarray
-    dgamma: np.ndarray
-    dstate: Optional[np.ndarray]
-    # error scales of an fp32 evaluation (see the C source), when asked for
-    cond_dx: Optional[np.ndarray] = None
-    cond_dtaps: Optional[np.ndarray] = None
-    cond_dgamma: Optional[np.ndarray] = None
-    cond_dstate: Optional[np.ndarray] = None
-
-
-def backward_one(x, cu_seqlens, taps, gamma, eps, state, state_idx, has_init, g, gs=None, *,
-                 cond=False, nthreads=1):
-    """Backward of ``prefill_one`` for the loss whose gradient is ``g`` = dLoss/dy (fp64
-    [T,H,D]) plus ``gs`` = dLoss/d(new state) (fp64 [N,W-1,H,D] or None). The chain rule through
-    the definition; the C source states each step."""
-    lib = _load()
-    taps = np.ascontiguousarray(taps, dtype=np.float32)
-    W, H, D = taps.shape
-    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
-    code = _dtype_code(x)
-    x, xs = _token_rows(x, H, D)
-    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
-    N = cu.shape[0] - 1
-    T = x.shape[0]
-    assert N >= 0 and cu[0] == 0 and cu[-1] <= T and np.all(np.diff(cu) >= 0)
-    sidx = np.ascontiguousarray(state_idx if state_idx is not None else np.arange(N), dtype=np.int64)
-    hinit = np.ascontiguousarray(has_init if has_init is not None else np.ones(N), dtype=np.uint8)
-    if W > 1 and state is not None:
-        state = np.ascontiguousarray(state)
-        assert state.dtype == x.dtype and state.shape[1:] == (W - 1, H, D)
-        n_state = state.shape[0]
-    else:
-        state, n_state = None, 0
-    g = np.ascontiguousarray(g, dtype=np.float64)
-    assert g.shape == (T, H, D)
-    if gs is not None and W > 1:
-        gs = np.ascontiguousarray(gs, dtype=np.float64)
-        assert gs.shape == (N, W - 1, H, D)
-    else:
-        gs = None
-    dx = np.zeros((T, H, D), np.float64)
-    dtaps = np.zeros((W, H, D), np.float64)
-    dgamma = np.zeros(D, np.float64)
-    dstate = np.zeros((N, W - 1, H, D), np.float64) if W > 1 else None
-    if cond:
-        cdx, cdt, cdg = np.zeros_like(dx), np.zeros_like(dtaps), np.zeros_like(dgamma)
-        cds = np.zeros_like(dstate) if dstate is not None else None
-    else:
-        cdx = cdt = cdg = cds = None
-    rc = lib.sc_oracle_backward(code, H, D, W, N, _ptr(cu), _ptr(x), xs, _ptr(taps), _ptr(gamma),
-                                float(eps), _ptr(state), n_state, _ptr(sidx), _ptr(hinit), _ptr(g),
-                                _ptr(gs), _ptr(dx), _ptr(dtaps), _ptr(dgamma), _ptr(dstate),
-                                _ptr(cdx), _ptr(cdt), _ptr(cdg), _ptr(cds), int(nthreads))
-    if rc != 0:
-        raise ValueError("oracle backward rejected its arguments")
-    return Grads(dx, dtaps, dgamma, dstate, cdx, cdt, cdg, cds)
-
-
-def fused_backward(k, v, cu_seqlens, k_taps, v_taps, k_gamma, v_gamma, eps, k_state, v_state,
-                   state_idx, has_init, gk, gv, gsk=None, gsv=None, *, cond=False, nthreads=1):
-    """``backward_one`` for K and V: returns (Grads of K, Grads of V)."""
-    a = backward_one(k, cu_seqlens, k_taps, k_gamma, eps, k_state, state_idx, has_init, gk, gsk,
-                     cond=cond, nthreads=nthreads)
-    b = backward_one(v, cu_seqlens, v_taps, v_gamma, eps, v_state, state_idx, has_init, gv, gsv,
-                     cond=cond, nthreads=nthreads)
-    return a, b
-
-
 def verify_snapshots(x, cu_seqlens, state, state_idx, width, max_tokens):
     """snapshots[s, i] = rows e[i+1 .. i+W-1] of e = [initial window, rows of sequence s], i.e. the
     conv state after its first i+1 tokens, as bit copies; written for i < min(L_s, max_tokens),
@@ -433,6 +361,86 @@ def mxfp8_dequantize(codes, scales):
     vals = e4m3_decode(c).reshape(*c.shape[:-1], D // MX_BLOCK, MX_BLOCK)
     x = np.ldexp(1.0, np.asarray(scales, np.int64) - 127)[..., None]
     return (vals * x).reshape(c.shape)
+
+
+# ---------------------------------------------------------------------------------------------
+# Backward: the gradients of the step for training (the English news item on SGLang/Miles
+# Inkling support, paragraph 3: the RL trainer runs the model with train/infer-consistent
+# kernels). The arithmetic -- the chain rule through the definition, step by step -- is
+# sc_oracle_backward in shortconv_oracle.c, whose header states each step.
+# ---------------------------------------------------------------------------------------------
+@dataclass
+class Grads:
+    """Gradients of one tensor's step (all fp64): dx [T,H,D], dtaps [W,H,D], dgamma [D], and
+    dstate [N,W-1,H,D] (None when W == 1), the gradient of each sequence's initial window rows
+    (zero for a sequence that started from zeros)."""
+    dx: np.ndarray
+    dtaps: np.ndarray
+    dgamma: np.ndarray
+    dstate: Optional[np.ndarray]
+    # error scales of an fp32 evaluation (see the C source), when asked for
+    cond_dx: Optional[np.ndarray] = None
+    cond_dtaps: Optional[np.ndarray] = None
+    cond_dgamma: Optional[np.ndarray] = None
+    cond_dstate: Optional[np.ndarray] = None
+
+
+def backward_one(x, cu_seqlens, taps, gamma, eps, state, state_idx, has_init, g, gs=None, *,
+                 cond=False, nthreads=1):
+    """Backward of ``prefill_one`` for the loss whose gradient is ``g`` = dLoss/dy (fp64
+    [T,H,D]) plus ``gs`` = dLoss/d(new state) (fp64 [N,W-1,H,D] or None). The chain rule through
+    the definition; the C source states each step."""
+    lib = _load()
+    taps = np.ascontiguousarray(taps, dtype=np.float32)
+    W, H, D = taps.shape
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    code = _dtype_code(x)
+    x, xs = _token_rows(x, H, D)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    N = cu.shape[0] - 1
+    T = x.shape[0]
+    assert N >= 0 and cu[0] == 0 and cu[-1] <= T and np.all(np.diff(cu) >= 0)
+    sidx = np.ascontiguousarray(state_idx if state_idx is not None else np.arange(N), dtype=np.int64)
+    hinit = np.ascontiguousarray(has_init if has_init is not None else np.ones(N), dtype=np.uint8)
+    if W > 1 and state is not None:
+        state = np.ascontiguousarray(state)
+        assert state.dtype == x.dtype and state.shape[1:] == (W - 1, H, D)
+        n_state = state.shape[0]
+    else:
+        state, n_state = None, 0
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    assert g.shape == (T, H, D)
+    if gs is not None and W > 1:
+        gs = np.ascontiguousarray(gs, dtype=np.float64)
+        assert gs.shape == (N, W - 1, H, D)
+    else:
+        gs = None
+    dx = np.zeros((T, H, D), np.float64)
+    dtaps = np.zeros((W, H, D), np.float64)
+    dgamma = np.zeros(D, np.float64)
+    dstate = np.zeros((N, W - 1, H, D), np.float64) if W > 1 else None
+    if cond:
+        cdx, cdt, cdg = np.zeros_like(dx), np.zeros_like(dtaps), np.zeros_like(dgamma)
+        cds = np.zeros_like(dstate) if dstate is not None else None
+    else:
+        cdx = cdt = cdg = cds = None
+    rc = lib.sc_oracle_backward(code, H, D, W, N, _ptr(cu), _ptr(x), xs, _ptr(taps), _ptr(gamma),
+                                float(eps), _ptr(state), n_state, _ptr(sidx), _ptr(hinit), _ptr(g),
+                                _ptr(gs), _ptr(dx), _ptr(dtaps), _ptr(dgamma), _ptr(dstate),
+                                _ptr(cdx), _ptr(cdt), _ptr(cdg), _ptr(cds), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle backward rejected its arguments")
+    return Grads(dx, dtaps, dgamma, dstate, cdx, cdt, cdg, cds)
+
+
+def fused_backward(k, v, cu_seqlens, k_taps, v_taps, k_gamma, v_gamma, eps, k_state, v_state,
+                   state_idx, has_init, gk, gv, gsk=None, gsv=None, *, cond=False, nthreads=1):
+    """``backward_one`` for K and V: returns (Grads of K, Grads of V)."""
+    a = backward_one(k, cu_seqlens, k_taps, k_gamma, eps, k_state, state_idx, has_init, gk, gsk,
+                     cond=cond, nthreads=nthreads)
+    b = backward_one(v, cu_seqlens, v_taps, v_gamma, eps, v_state, state_idx, has_init, gv, gsv,
+                     cond=cond, nthreads=nthreads)
+    return a, b
 
 
 # ---------------------------------------------------------------------------------------------
