@@ -2,6 +2,7 @@
 """Benchmark of the fused ShortConv K/V step on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload varlen_prefill] [--no-cpu-baseline]
+                    [--no-decode] [--no-extras] [--only main|decode|mxfp8|verify|backward]
 
 A step is one call of the fused step over one batch of the workload (for the default workload:
 8 packed sequences of U{512..4096} tokens, 8 KV heads x 128, W = 4, bf16 rows with fp32
@@ -13,10 +14,15 @@ The K timed launches are captured once into a HIP graph and replayed (host launc
 otherwise pace short kernels); --eager launches them from Python instead.
 
 Prints ONE JSON line: tokens/s over the timed steps (wall clock between two device
-synchronizations), the average duration of one fused launch (device time between HIP events
-recorded on the launch stream before the first and after the last launch, divided by K),
-algorithmic HBM bytes / that duration against the 8 TB/s peak, the same for the decode step
-(256 sequences x 1 token), and the fp64 CPU oracle timed on host cores.
+synchronizations), the average duration of one step (device time between HIP events recorded on
+the launch stream before the first and after the last launch, divided by K), algorithmic HBM
+bytes / that duration against the 8 TB/s peak (`roofline`, with the counter-measured `traffic`
+while profiles/ holds counters for these kernel sources), a same-bytes copy (`copy_ceiling`), the
+same measurement for the decode step (256 sequences x 1 token), the workload with MXFP8 cache
+rows, a speculative verify + commit step and the backward of the prefill, and the fp64 CPU
+oracle timed on host cores (`cpu_baseline`). --only NAME runs one measurement and prints a
+line of text instead (for profiling and sweeps); --workload picks another of the five
+configurations.
 
 Profiling helpers (run under rocprofv3, then summarize):
     --calibrate-copy         also run a plain device copy of known size (counter calibration)
