@@ -576,8 +576,11 @@ def main():
         dm = measure(torch, wd, args.steps, args.warmup,
                      reseed=lambda r: workloads.config(3, seed=args.seed + 1000 * r),
                      graph=graph)
+        dceil = copy_ceiling(torch, dm["algorithmic_bytes"], args.steps, args.warmup)
         extra["decode"] = {"workload": "decode", "recipe": wd.recipe, **_round(dm),
-                           "frac_of_hbm_peak": dm["achieved_GBps"] / HBM_PEAK_GBPS}
+                           "frac_of_hbm_peak": dm["achieved_GBps"] / HBM_PEAK_GBPS,
+                           "copy_ceiling_GBps": dceil["GBps"],
+                           "kernel_over_copy": dm["achieved_GBps"] / dceil["GBps"]}
     if not args.no_extras:
         mm = measure(torch, w, args.steps, args.warmup, reseed_main, graph, cache="mxfp8")
         extra["mxfp8_cache"] = {"workload": w.name, **_round(mm),
