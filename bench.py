@@ -46,7 +46,6 @@ MALL_BYTES = 256 << 20          # MI355X Infinity Cache
 KERNEL_SRC = [os.path.join(ROOT, "causal_short_convolution_amd", "csrc", f)
               for f in ("kernels.hip", "device_common.h")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "varlen_bf16_all_kernels_traffic.md")
-WORKLOADS = {"tiny_ref": 1, "varlen_prefill": 2, "decode": 3, "long_prefill": 4, "mixed": 5}
 COPY_BYTES = 512 << 20          # calibration copy: 512 MiB read + 512 MiB written
 KERNELS = ("prefill_kernel", "decode_kernel", "verify_kernel", "commit_kernel",
            "mx_quantize_kernel", "backward_kernel", "backward_chunk_kernel", "backward_final_kernel")
@@ -132,7 +131,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="varlen_prefill", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="varlen_prefill",
+                    choices=["tiny_ref", "varlen_prefill", "decode", "long_prefill", "mixed"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-extras", action="store_true",
@@ -533,9 +533,9 @@ def main():
         summarize_profile(args.summarize_profile)
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the step shards with no communication across heads or sequences; see the design "
-              "notes)", file=sys.stderr)
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported (the step "
+              "shards with no communication across heads or sequences, so a multi-GPU run would "
+              "be this run per GPU)", file=sys.stderr)
         return 2
     from causal_short_convolution_amd import _binding
     if not os.path.exists(_binding.LIBRARY_PATH):
@@ -547,7 +547,7 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
 
-    n = WORKLOADS[args.workload]
+    n = args.workload
     w = workloads.config(n, seed=args.seed)
     has_decode = any(st.kind == "decode" for st in w.steps)
     reseed_main = ((lambda r: workloads.config(n, seed=args.seed + 1000 * r))
@@ -560,8 +560,8 @@ def main():
         elif args.only == "mxfp8":
             m = measure(torch, w, args.steps, args.warmup, reseed_main, graph, cache="mxfp8")
         elif args.only == "decode":
-            m = measure(torch, workloads.config(3, seed=args.seed), args.steps, args.warmup,
-                        lambda r: workloads.config(3, seed=args.seed + 1000 * r), graph)
+            m = measure(torch, workloads.config("decode", seed=args.seed), args.steps, args.warmup,
+                        lambda r: workloads.config("decode", seed=args.seed + 1000 * r), graph)
         elif args.only == "backward":
             m = measure_backward(torch, w, args.steps, args.warmup, graph)
         else:
@@ -572,9 +572,9 @@ def main():
     main_m = measure(torch, w, args.steps, args.warmup, reseed_main, graph)
     extra = {}
     if not args.no_decode and args.workload != "decode":
-        wd = workloads.config(3, seed=args.seed)
+        wd = workloads.config("decode", seed=args.seed)
         dm = measure(torch, wd, args.steps, args.warmup,
-                     reseed=lambda r: workloads.config(3, seed=args.seed + 1000 * r),
+                     reseed=lambda r: workloads.config("decode", seed=args.seed + 1000 * r),
                      graph=graph)
         dceil = copy_ceiling(torch, dm["algorithmic_bytes"], args.steps, args.warmup)
         extra["decode"] = {"workload": "decode", "recipe": wd.recipe, **_round(dm),

@@ -34,7 +34,7 @@ def sha(*arrays):
 
 
 def snapshot():
-    w = workloads.config(1)
+    w = workloads.config("tiny_ref")
     st = w.steps[0]
     r = oracle.fused_prefill(st.k, st.v, st.cu_seqlens, w.k_taps, w.v_taps, w.k_gamma, w.v_gamma,
                              w.eps, w.k_state, w.v_state, st.state_idx, st.has_init,

@@ -173,13 +173,13 @@ def test_backward_is_deterministic():
     case.check(a)
 
 
-@pytest.mark.parametrize("n", [2, 4])
-def test_backward_reference_workload_shapes(n):
+@pytest.mark.parametrize("name", ["varlen_prefill", "long_prefill"])
+def test_backward_reference_workload_shapes(name):
     """The varlen prefill and long prefill workloads, at full size."""
-    spec = workloads.config_spec(n)
+    spec = workloads.config_spec(name)
     case = BwdCase(None, None, None, None, None, None, seed=None, spec=spec)
     worst = case.check()
-    print(f"config {n} backward worst error/bound: {worst}")
+    print(f"{name} backward worst error/bound: {worst}")
 
 
 def test_backward_without_sequences_zeroes_parameter_gradients():

@@ -32,11 +32,11 @@ def _run_and_judge(w):
 # ------------------------------------------------------------------------------------------------
 # The five reference workloads at full size
 # ------------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
-def test_reference_workload(n):
-    w = workloads.config(n)
+@pytest.mark.parametrize("name", workloads.CONFIG_NAMES)
+def test_reference_workload(name):
+    w = workloads.config(name)
     rep = _run_and_judge(w)
-    print(f"config {n} ({w.name}): rows={rep['rows']} worst={rep['worst']:.3f} "
+    print(f"{w.name}: rows={rep['rows']} worst={rep['worst']:.3f} "
           f"max_rel_well_conditioned={rep['max_rel_well_conditioned']:.3e}", flush=True)
     assert rep["rows"] == w.tokens
 
@@ -119,7 +119,7 @@ def test_non_default_stream():
 
 
 def test_empty_calls_are_noops():
-    w = workloads.config(1)
+    w = workloads.config("tiny_ref")
     dw = DeviceWorkload(w)
     e_rows = torch.empty((0, 1, 64), dtype=torch.float32, device=DEV)
     e_i64 = torch.empty(0, dtype=torch.int64, device=DEV)
@@ -135,7 +135,7 @@ def test_empty_calls_are_noops():
 
 
 def test_rejects_bad_arguments_without_launch():
-    w = workloads.config(1)
+    w = workloads.config("tiny_ref")
     dw = DeviceWorkload(w)
     d = dw.steps[0]
     with pytest.raises(ShortConvError, match="SC_ERR_UNSUPPORTED"):

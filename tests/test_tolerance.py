@@ -47,7 +47,7 @@ def _check(w, st, plant=None):
 
 
 def test_fp32_model_passes_config1():
-    w = workloads.config(1)
+    w = workloads.config("tiny_ref")
     r = _check(w, w.steps[0])
     assert r["ok"], r
     assert r["max_rel_well_conditioned"] <= oracle.TOL["f32"]
@@ -63,7 +63,7 @@ def test_fp32_model_passes_bf16_with_outliers():
 
 
 def test_planted_errors_fail():
-    w = workloads.config(1)
+    w = workloads.config("tiny_ref")
     st = w.steps[0]
 
     def bump(g):
@@ -93,7 +93,7 @@ def test_planted_errors_fail():
 
 
 def test_nonfinite_fails():
-    w = workloads.config(1)
+    w = workloads.config("tiny_ref")
 
     def nan(g):
         g = g.copy()

@@ -21,9 +21,9 @@ def _digest(w):
 
 
 def test_same_seed_same_inputs_other_seed_other_inputs():
-    for n in (1, 2, 3):
-        assert _digest(workloads.config(n, seed=0)) == _digest(workloads.config(n, seed=0))
-        assert _digest(workloads.config(n, seed=0)) != _digest(workloads.config(n, seed=1))
+    for name in ("tiny_ref", "varlen_prefill", "decode"):
+        a, b = workloads.config(name, seed=0), workloads.config(name, seed=1)
+        assert _digest(a) == _digest(workloads.config(name, seed=0)) and _digest(a) != _digest(b)
 
 
 def test_streams_are_independent():
@@ -39,7 +39,7 @@ def test_streams_are_independent():
 
 
 def test_config_shapes_and_structure():
-    w2 = workloads.config(2)
+    w2 = workloads.config("varlen_prefill")
     st = w2.steps[0]
     lens = np.diff(st.cu_seqlens)
     assert st.num_seqs == 8 and ((lens >= 512) & (lens <= 4096)).all() and w2.tokens == 17060
@@ -48,13 +48,13 @@ def test_config_shapes_and_structure():
     assert len(np.unique(st.slot_mapping)) == st.tokens and st.slot_mapping.max() < w2.num_slots
     first = st.slot_mapping[:16]
     assert (np.diff(first) == 1).all() and first[0] % 16 == 0
-    w3 = workloads.config(3)
+    w3 = workloads.config("decode")
     d = w3.steps[0]
     assert d.kind == "decode" and d.tokens == 256 and len(np.unique(d.state_idx)) == 256
     # the large ones by their recipes (building them draws ~10^9 numbers)
-    s4 = workloads.config_spec(4)
+    s4 = workloads.config_spec("long_prefill")
     assert s4.W == 8 and list(s4.prefill_lens) == [131072] and s4.outlier_p == 0.01
-    s5 = workloads.config_spec(5)
+    s5 = workloads.config_spec("mixed")
     assert s5.H == 16 and list(s5.prefill_lens) == [2048] * 64 and len(s5.decode_ctx) == 512
     assert all(s5.has_init) and all(p % 2048 == 0 and 2048 <= p <= 2048 * 15
                                     for p in s5.prefill_start)

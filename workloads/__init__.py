@@ -226,55 +226,63 @@ def build(spec: Spec) -> Workload:
 
 
 # ---------------------------------------------------------------------------------------------
-# The five reference workloads. Shapes, distributions and paging follow the benchmark's config list;
-# where a config leaves a draw unstated, the choice below is stated in its recipe string.
+# The five measured workloads: a tiny fp32 reference, a packed variable-length prefill batch, a
+# decode batch, one long prefill at width 8, and a mixed chunked-prefill + decode step. Every
+# draw a workload leaves open is stated in its recipe string.
 # ---------------------------------------------------------------------------------------------
-CONFIG_NAMES = {1: "tiny_ref", 2: "varlen_prefill", 3: "decode", 4: "long_prefill", 5: "mixed"}
+# The five workloads, in order; each one's random streams are keyed by its tag (1..5).
+CONFIG_NAMES = ("tiny_ref", "varlen_prefill", "decode", "long_prefill", "mixed")
+_TAG = {name: i + 1 for i, name in enumerate(CONFIG_NAMES)}
 
 
-def config_spec(n: int, seed: int = 0) -> Spec:
-    if n == 1:
-        return Spec(name="tiny_ref", dtype="f32", H=1, D=64, W=4, seed=seed, tag=1,
-                    prefill_lens=[64], has_init=[1], state_init="zero", contiguous_cache=True)
-    if n == 2:
-        lens = rng(seed, 2, _S_LENS).integers(512, 4096, size=8, endpoint=True)
-        return Spec(name="varlen_prefill", dtype="bf16", H=8, D=128, W=4, seed=seed, tag=2,
+def config_spec(name: str, seed: int = 0) -> Spec:
+    """The recipe of one of the five workloads (CONFIG_NAMES), drawn with `seed`."""
+    if name not in _TAG:
+        raise ValueError(f"unknown workload {name!r}; one of {CONFIG_NAMES}")
+    t = _TAG[name]
+    if name == "tiny_ref":
+        return Spec(name=name, dtype="f32", H=1, D=64, W=4, seed=seed, tag=t, prefill_lens=[64],
+                    has_init=[1], state_init="zero", contiguous_cache=True)
+    if name == "varlen_prefill":
+        lens = rng(seed, t, _S_LENS).integers(512, 4096, size=8, endpoint=True)
+        return Spec(name=name, dtype="bf16", H=8, D=128, W=4, seed=seed, tag=t,
                     prefill_lens=lens.tolist(), has_init=[0] * 8, block_size=16)
-    if n == 3:
-        ctx = rng(seed, 3, _S_DEC_CTX).integers(1, 32768, size=256, endpoint=True)
-        return Spec(name="decode", dtype="bf16", H=8, D=128, W=4, seed=seed, tag=3,
+    if name == "decode":
+        ctx = rng(seed, t, _S_DEC_CTX).integers(1, 32768, size=256, endpoint=True)
+        return Spec(name=name, dtype="bf16", H=8, D=128, W=4, seed=seed, tag=t,
                     decode_ctx=ctx.tolist(), block_size=64)
-    if n == 4:
-        return Spec(name="long_prefill", dtype="bf16", H=8, D=128, W=8, seed=seed, tag=4,
+    if name == "long_prefill":
+        return Spec(name=name, dtype="bf16", H=8, D=128, W=8, seed=seed, tag=t,
                     prefill_lens=[131072], has_init=[0], block_size=64, outlier_p=0.01,
                     outlier_mul=50.0)
-    if n == 5:
-        g = rng(seed, 5, _S_START)
-        starts = 2048 * g.integers(1, 15, size=64, endpoint=True)
-        ctx = rng(seed, 5, _S_DEC_CTX).integers(1, 32768, size=512, endpoint=True)
-        return Spec(name="mixed", dtype="bf16", H=16, D=128, W=4, seed=seed, tag=5,
-                    prefill_lens=[2048] * 64, prefill_start=starts.tolist(), has_init=[1] * 64,
-                    decode_ctx=ctx.tolist(), block_size=16)
-    raise ValueError(f"unknown config {n}")
+    g = rng(seed, t, _S_START)  # mixed
+    starts = 2048 * g.integers(1, 15, size=64, endpoint=True)
+    ctx = rng(seed, t, _S_DEC_CTX).integers(1, 32768, size=512, endpoint=True)
+    return Spec(name=name, dtype="bf16", H=16, D=128, W=4, seed=seed, tag=t,
+                prefill_lens=[2048] * 64, prefill_start=starts.tolist(), has_init=[1] * 64,
+                decode_ctx=ctx.tolist(), block_size=16)
 
 
-def config(n: int, seed: int = 0) -> Workload:
-    w = build(config_spec(n, seed))
-    w.recipe = RECIPES[n]
+def config(name: str, seed: int = 0) -> Workload:
+    """One of the five workloads (CONFIG_NAMES), built, with its recipe string."""
+    w = build(config_spec(name, seed))
+    w.recipe = RECIPES[name]
     return w
 
 
 RECIPES = {
-    1: "1 seq x 64 tokens, H=1, D=64, W=4, fp32; K,V~N(0,1); taps~N(0,1/W); gamma=1+0.1N(0,1); "
-       "zero initial state; slot i = token i",
-    2: "8 seqs, lengths U{512..4096}, H=8, D=128, W=4, bf16; K,V~N(0,1); fresh (zero) state; "
-       "paged cache, block 16, one random permutation of the pool as block tables",
-    3: "256 decodes, H=8, D=128, W=4, bf16; state rows~N(0,1); state slots permuted; "
-       "context U{1..32768}; paged cache, block 64, permuted block tables",
-    4: "1 seq x 131072 tokens, H=8, D=128, W=8, bf16; K,V~N(0,1) with each entry x50 w.p. 0.01; "
-       "fresh state; paged cache, block 64, permuted block table",
-    5: "64 chunks x 2048 tokens resuming at 2048*U{1..15} from state~N(0,1) + 512 decodes "
-       "(context U{1..32768}), H=16, D=128, W=4, bf16; paged cache, block 16, permuted tables",
+    "tiny_ref": "1 seq x 64 tokens, H=1, D=64, W=4, fp32; K,V~N(0,1); taps~N(0,1/W); "
+                "gamma=1+0.1N(0,1); zero initial state; slot i = token i",
+    "varlen_prefill": "8 seqs, lengths U{512..4096}, H=8, D=128, W=4, bf16; K,V~N(0,1); fresh "
+                      "(zero) state; paged cache, block 16, one random permutation of the pool "
+                      "as block tables",
+    "decode": "256 decodes, H=8, D=128, W=4, bf16; state rows~N(0,1); state slots permuted; "
+              "context U{1..32768}; paged cache, block 64, permuted block tables",
+    "long_prefill": "1 seq x 131072 tokens, H=8, D=128, W=8, bf16; K,V~N(0,1) with each entry x50 "
+                    "w.p. 0.01; fresh state; paged cache, block 64, permuted block table",
+    "mixed": "64 chunks x 2048 tokens resuming at 2048*U{1..15} from state~N(0,1) + 512 decodes "
+             "(context U{1..32768}), H=16, D=128, W=4, bf16; paged cache, block 16, permuted "
+             "tables",
 }
 
 
