@@ -70,7 +70,8 @@ class BwdCase:
         self.gsv = _stored_normal(g, (N, R, w.H, w.D), w.dtype) if (gs and R > 0) else None
         self.want_dstate = dstate and R > 0
 
-    def run_gpu(self):
+    def prepare(self):
+        """Device inputs and sentinel-filled outputs of one backward call."""
         w, st = self.w, self.st
         R, N, T = self.W - 1, st.num_seqs, st.tokens
         dt = TORCH_DT[self.dtype]
@@ -82,29 +83,43 @@ class BwdCase:
             t.view(bits).fill_(sentinel)
             return t
 
-        dk, dv = filled((T, self.H, self.D)), filled((T, self.H, self.D))
-        dks = dvs = None
+        b = dict(k=rows_to_dev(st.k), v=rows_to_dev(st.v),
+                 cu=to_dev(st.cu_seqlens.astype(np.int32)), kt=to_dev(w.k_taps),
+                 vt=to_dev(w.v_taps), kg=to_dev(w.k_gamma), vg=to_dev(w.v_gamma),
+                 ks=to_dev(w.k_state), vs=to_dev(w.v_state),
+                 sidx=to_dev(st.state_idx.astype(np.int32)),
+                 hinit=to_dev(st.has_init.astype(np.uint8)), dyk=to_dev(self.dyk),
+                 dyv=to_dev(self.dyv), gsk=to_dev(self.gsk), gsv=to_dev(self.gsv),
+                 dk=filled((T, self.H, self.D)), dv=filled((T, self.H, self.D)),
+                 dks=filled((N, R, self.H, self.D)) if self.want_dstate else None,
+                 dvs=filled((N, R, self.H, self.D)) if self.want_dstate else None,
+                 dkt=torch.full((self.W, self.H, self.D), float("nan"), device=DEV),
+                 dvt=torch.full((self.W, self.H, self.D), float("nan"), device=DEV),
+                 dkg=torch.full((self.D,), float("nan"), device=DEV),
+                 dvg=torch.full((self.D,), float("nan"), device=DEV))
+        return b
+
+    def launch(self, b, workspace=None):
+        shortconv_kv_backward(b["k"], b["v"], b["cu"], b["kt"], b["vt"], b["kg"], b["vg"],
+                              self.w.eps, b["ks"], b["vs"], b["sidx"], b["hinit"], b["dyk"],
+                              b["dyv"], b["dk"], b["dv"], b["dkt"], b["dvt"], b["dkg"], b["dvg"],
+                              dstate_out=(b["gsk"], b["gsv"]), dstate_in=(b["dks"], b["dvs"]),
+                              workspace=workspace)
+
+    def collect(self, b):
+        out = dict(dk=to_host(b["dk"], self.dtype), dv=to_host(b["dv"], self.dtype),
+                   dkt=b["dkt"].cpu().numpy(), dvt=b["dvt"].cpu().numpy(),
+                   dkg=b["dkg"].cpu().numpy(), dvg=b["dvg"].cpu().numpy())
         if self.want_dstate:
-            dks, dvs = filled((N, R, self.H, self.D)), filled((N, R, self.H, self.D))
-        dkt = torch.full((self.W, self.H, self.D), float("nan"), device=DEV)
-        dvt = torch.full_like(dkt, float("nan"))
-        dkg = torch.full((self.D,), float("nan"), device=DEV)
-        dvg = torch.full_like(dkg, float("nan"))
-        shortconv_kv_backward(
-            rows_to_dev(st.k), rows_to_dev(st.v), to_dev(st.cu_seqlens.astype(np.int32)),
-            to_dev(w.k_taps), to_dev(w.v_taps), to_dev(w.k_gamma), to_dev(w.v_gamma), w.eps,
-            to_dev(w.k_state), to_dev(w.v_state), to_dev(st.state_idx.astype(np.int32)),
-            to_dev(st.has_init.astype(np.uint8)), to_dev(self.dyk), to_dev(self.dyv), dk, dv,
-            dkt, dvt, dkg, dvg, dstate_out=(to_dev(self.gsk), to_dev(self.gsv)),
-            dstate_in=(dks, dvs))
-        torch.cuda.synchronize()
-        out = dict(dk=to_host(dk, self.dtype), dv=to_host(dv, self.dtype),
-                   dkt=dkt.cpu().numpy(), dvt=dvt.cpu().numpy(), dkg=dkg.cpu().numpy(),
-                   dvg=dvg.cpu().numpy())
-        if self.want_dstate:
-            out["dks"] = to_host(dks, self.dtype)
-            out["dvs"] = to_host(dvs, self.dtype)
+            out["dks"] = to_host(b["dks"], self.dtype)
+            out["dvs"] = to_host(b["dvs"], self.dtype)
         return out
+
+    def run_gpu(self):
+        b = self.prepare()
+        self.launch(b)
+        torch.cuda.synchronize()
+        return self.collect(b)
 
     def oracle(self):
         w, st = self.w, self.st
@@ -215,3 +230,31 @@ def test_backward_rejects_short_workspace():
                               to_dev(st.state_idx.astype(np.int32)),
                               to_dev(st.has_init.astype(np.uint8)), dk, dk, dk.clone(), dk.clone(),
                               g, g.clone(), gm, gm.clone(), workspace=ws)
+
+
+def test_backward_graph_replay_matches_eager():
+    """The backward's launches captured in a HIP graph: every replay, with the outputs cleared
+    eagerly in between, gives the eager run's bits (the sums' workspace included in the graph)."""
+    case = BwdCase("bf16", 8, 128, 4, [300, 3, 0, 40], [1, 0, 1, 1], seed=12)
+    eager = case.run_gpu()
+    b = case.prepare()
+    st = case.st
+    need = shortconv_kv_backward_workspace_size(st.tokens, st.num_seqs, case.H, case.D, case.W,
+                                                torch.bfloat16)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    case.launch(b, ws)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        case.launch(b, ws)
+    for _ in range(3):
+        for key in ("dk", "dv", "dks", "dvs", "dkt", "dvt", "dkg", "dvg"):
+            b[key].zero_()
+        ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = case.collect(b)
+        for key in eager:
+            assert np.array_equal(np.ascontiguousarray(got[key]).view(np.uint8),
+                                  np.ascontiguousarray(eager[key]).view(np.uint8)), key

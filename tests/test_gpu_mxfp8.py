@@ -224,3 +224,48 @@ def test_fused_mx_bf16_equals_quantized_plain_rows_but_double_rounding():
         assert (step[diff] <= gap[diff] * (1 + 1e-12)).all(), "a flipped code is more than a step"
         flips += int(diff.sum()) + int(bad_scale.sum())
     print(f"double-rounding flips: {flips}")
+
+
+def test_mx_graph_replay_matches_eager():
+    """MXFP8 prefill + decode captured in a HIP graph: every replay (state restored eagerly in
+    between) writes the eager run's code and scale bytes."""
+    spec = workloads.Spec(dtype="bf16", H=8, D=128, W=4, seed=71, prefill_lens=[90, 5, 33],
+                          has_init=[1, 0, 1], decode_ctx=[12, 40])
+    w = workloads.build(spec)
+    plain, mx = _fused_pair(w)  # mx holds the eager MXFP8 results
+    eager = [t.cpu().numpy() for t in (mx.k_codes, mx.v_codes, mx.k_scales, mx.v_scales)]
+    mx2 = DeviceWorkload(w, caches=False)
+    for name in ("k_codes", "v_codes", "k_scales", "v_scales"):
+        setattr(mx2, name, torch.zeros_like(getattr(mx, name)))
+    k0, v0 = mx2.k_state.clone(), mx2.v_state.clone()
+
+    def step():
+        for d in mx2.steps:
+            if d["kind"] == "prefill":
+                shortconv_kv_prefill_mxfp8(d["k"], d["v"], d["cu"], mx2.k_taps, mx2.v_taps,
+                                           mx2.k_gamma, mx2.v_gamma, w.eps, mx2.k_state,
+                                           mx2.v_state, d["sidx"], d["hinit"], d["slot"],
+                                           mx2.k_codes, mx2.v_codes, mx2.k_scales, mx2.v_scales)
+            else:
+                shortconv_kv_decode_mxfp8(d["k"], d["v"], mx2.k_taps, mx2.v_taps, mx2.k_gamma,
+                                          mx2.v_gamma, w.eps, mx2.k_state, mx2.v_state,
+                                          d["sidx"], d["slot"], mx2.k_codes, mx2.v_codes,
+                                          mx2.k_scales, mx2.v_scales)
+
+    step()  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    rows = _written_slots(w)
+    for _ in range(3):
+        mx2.k_state.copy_(k0)
+        mx2.v_state.copy_(v0)
+        for name in ("k_codes", "v_codes", "k_scales", "v_scales"):
+            getattr(mx2, name).zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.cpu().numpy() for t in (mx2.k_codes, mx2.v_codes, mx2.k_scales, mx2.v_scales)]
+        for a, b in zip(got, eager):
+            assert np.array_equal(a[rows], b[rows])

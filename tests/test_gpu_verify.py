@@ -150,3 +150,53 @@ def test_speculative_rounds_match_prefill_of_accepted_tokens():
                                       base.eps, base.k_state, base.steps[0].state_idx[s:s + 1],
                                       np.array([1]))
         assert np.array_equal(got[base.steps[0].state_idx[s]], ns[0]), f"sequence {s}"
+
+
+def test_verify_commit_graph_replay_matches_eager():
+    """Verify + commit captured in a HIP graph: every replay, with the pools, caches and
+    snapshots restored or cleared eagerly in between, gives the eager run's bits."""
+    lens = [4, 1, 0, 4, 3]
+    max_tokens = 4
+    w = _verify_workload("bf16", 8, 128, 4, lens, seed=21)
+    st = w.steps[0]
+    accepted = to_dev(np.array([3, 1, 0, 4, 2], np.int32))
+    dw = DeviceWorkload(w)
+    d = dw.steps[0]
+    ks, vs = _snap_buffer(w, st.num_seqs, max_tokens)
+    k0, v0 = dw.k_state.clone(), dw.v_state.clone()
+
+    def step():
+        shortconv_kv_verify(d["k"], d["v"], d["cu"], dw.k_taps, dw.v_taps, dw.k_gamma,
+                            dw.v_gamma, w.eps, dw.k_state, dw.v_state, d["sidx"], ks, vs,
+                            d["slot"], dw.k_cache, dw.v_cache)
+        shortconv_state_commit(ks, vs, d["cu"], st.tokens, accepted, dw.k_state, dw.v_state,
+                               d["sidx"], width=w.W, num_heads=w.H, head_dim=w.D)
+
+    def outputs():
+        return [to_host(t, "bf16") for t in (dw.k_cache, dw.v_cache, dw.k_state, dw.v_state,
+                                             ks, vs)]
+
+    step()
+    torch.cuda.synchronize()
+    eager = outputs()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        dw.k_state.copy_(k0)
+        dw.v_state.copy_(v0)
+        for t in (dw.k_cache, dw.v_cache, ks, vs):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = outputs()
+        rows = st.slot_mapping[st.slot_mapping >= 0]
+        for a, b in zip(got[:2], eager[:2]):
+            assert np.array_equal(a[rows], b[rows])
+        for name, a, b in zip(("k_state", "v_state"), got[2:4], eager[2:4]):
+            assert np.array_equal(a, b), name
+        for s, L in enumerate(lens):  # snapshots that exist (the rest were zeroed)
+            n = min(L, max_tokens)
+            for a, b in zip(got[4:], eager[4:]):
+                assert np.array_equal(a[s, :n], b[s, :n]), f"snapshots of sequence {s}"
