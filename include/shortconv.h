@@ -243,8 +243,9 @@ int shortconv_state_commit(const void* k_snap, const void* v_snap, int32_t max_t
  *  do not matter and on exit are unspecified. Calls that share a workspace must be ordered.
  * Numerics: fp32 arithmetic (the forward's c and r are recomputed the same way). d_taps and
  *  d_gamma are deterministic: each workgroup sums at most 4 tiles of at most 64 tokens per lane
- *  in fp32, its 4 waves in order, and a second kernel adds the workgroup partials in fp64 in a
- *  fixed order, rounding once to fp32.
+ *  in fp32, its 4 waves in order, and two further kernels add the workgroup partials in fp64 in
+ *  a fixed order (chunks of 64 partials, then the chunks, and for d_gamma the heads), rounding
+ *  once to fp32.
  * With num_seqs == 0 the parameter gradients are zero and nothing else is written.
  */
 int shortconv_kv_backward(const void* k, const void* v, int64_t k_tok_stride, int64_t v_tok_stride,
