@@ -712,6 +712,36 @@ def pin_backward_locality():
                     f"locality of dx (W={W}, seq {s}, token {p})"
 
 
+def pin_backward_chunked_equals_oneshot():
+    """Chunked training: splitting sequences into two chunks (the second resuming from the
+    first's new state) and feeding the second chunk's initial-window gradient to the first as
+    its new-state gradient gives the one-shot input, tap and gamma gradients."""
+    for W in (4, 2, 8):
+        w, st, g, gs = _bwd_case(W=W, D=64, lens=(40, 11), hin=(1, 0), seed=51)
+        one = oracle.backward_one(st.k, st.cu_seqlens, w.k_taps, w.k_gamma, w.eps, w.k_state,
+                                  st.state_idx, st.has_init, g, gs)
+        cut = (17, 5)  # split points inside each sequence
+        cu = st.cu_seqlens
+        idx1 = np.concatenate([np.arange(cu[s], cu[s] + cut[s]) for s in range(2)])
+        idx2 = np.concatenate([np.arange(cu[s] + cut[s], cu[s + 1]) for s in range(2)])
+        cu1 = np.array([0, cut[0], cut[0] + cut[1]])
+        cu2 = np.array([0, 40 - cut[0], 40 - cut[0] + 11 - cut[1]])
+        _, mid, _ = oracle.prefill_one(st.k[idx1], cu1, w.k_taps, w.k_gamma, w.eps, w.k_state,
+                                       st.state_idx, st.has_init)
+        second = oracle.backward_one(st.k[idx2], cu2, w.k_taps, w.k_gamma, w.eps, mid,
+                                     np.arange(2), np.ones(2, np.uint8), g[idx2], gs)
+        first = oracle.backward_one(st.k[idx1], cu1, w.k_taps, w.k_gamma, w.eps, w.k_state,
+                                    st.state_idx, st.has_init, g[idx1], second.dstate)
+        dx = np.zeros_like(one.dx)
+        dx[idx1], dx[idx2] = first.dx, second.dx
+        pairs = (("dx", dx, one.dx), ("dtaps", first.dtaps + second.dtaps, one.dtaps),
+                 ("dgamma", first.dgamma + second.dgamma, one.dgamma),
+                 ("dstate", first.dstate, one.dstate))
+        for name, a, b in pairs:
+            assert np.allclose(a, b, rtol=1e-11, atol=1e-11 * np.abs(b).max()), \
+                f"chunked {name} (W={W})"
+
+
 ALL_PINS = [
     pin_exact_rational,
     pin_torch_conv1d_rmsnorm,
@@ -734,4 +764,5 @@ ALL_PINS = [
     pin_backward_torch_autograd,
     pin_backward_invariants,
     pin_backward_locality,
+    pin_backward_chunked_equals_oneshot,
 ]

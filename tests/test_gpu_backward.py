@@ -258,3 +258,56 @@ def test_backward_graph_replay_matches_eager():
         for key in eager:
             assert np.array_equal(np.ascontiguousarray(got[key]).view(np.uint8),
                                   np.ascontiguousarray(eager[key]).view(np.uint8)), key
+
+
+@pytest.mark.parametrize("W", [4, 8])
+def test_chunked_backward_composes_to_oneshot(W):
+    """Chunked training on the GPU: the second chunk resumes from the first's new state; its
+    initial-window gradient is the first chunk's new-state gradient. The composed input, tap and
+    gamma gradients equal the oracle's one-shot ones within the one-shot error bound (fp32 I/O,
+    so the handed-over gradient is rounded at fp32 precision)."""
+    case = BwdCase("f32", 4, 128, W, [90, 37], [1, 0], seed=81 + W)
+    w, st = case.w, case.st
+    cu = st.cu_seqlens
+    cut = (50, 9)
+    idx1 = np.concatenate([np.arange(cu[s], cu[s] + cut[s]) for s in range(2)])
+    idx2 = np.concatenate([np.arange(cu[s] + cut[s], cu[s + 1]) for s in range(2)])
+    cu1 = np.array([0, cut[0], cut[0] + cut[1]], np.int32)
+    cu2 = np.array([0, 90 - cut[0], 90 - cut[0] + 37 - cut[1]], np.int32)
+    _, mid, _ = oracle.prefill_one(st.k[idx1], cu1, w.k_taps, w.k_gamma, w.eps, w.k_state,
+                                   st.state_idx, st.has_init)
+    H, D, R = case.H, case.D, W - 1
+
+    def run(x, cuv, pool, sidx, hinit, dy, gs):
+        n = len(cuv) - 1
+        T = x.shape[0]
+        xd = to_dev(np.ascontiguousarray(x))
+        dx = torch.empty((T, H, D), device=DEV)
+        dst = torch.empty((n, R, H, D), device=DEV)
+        dt, dtv = torch.empty((W, H, D), device=DEV), torch.empty((W, H, D), device=DEV)
+        dg, dgv = torch.empty(D, device=DEV), torch.empty(D, device=DEV)
+        dv_dummy = torch.empty_like(dx)
+        dst_v = torch.empty_like(dst)
+        gsd = to_dev(np.ascontiguousarray(gs, np.float32)) if gs is not None else None
+        shortconv_kv_backward(xd, xd, to_dev(cuv), to_dev(w.k_taps), to_dev(w.k_taps),
+                              to_dev(w.k_gamma), to_dev(w.k_gamma), w.eps, to_dev(pool),
+                              to_dev(pool), to_dev(sidx.astype(np.int32)),
+                              to_dev(hinit.astype(np.uint8)), to_dev(dy), to_dev(dy), dx,
+                              dv_dummy, dt, dtv, dg, dgv, dstate_out=(gsd, gsd),
+                              dstate_in=(dst, dst_v))
+        torch.cuda.synchronize()
+        return dx.cpu().numpy(), dt.cpu().numpy(), dg.cpu().numpy(), dst.cpu().numpy()
+
+    dyk = case.dyk
+    gs = oracle.widen(case.gsk)
+    dx2, dt2, dg2, ds2 = run(st.k[idx2], cu2, mid, np.arange(2), np.ones(2), dyk[idx2], gs)
+    dx1, dt1, dg1, ds1 = run(st.k[idx1], cu1, w.k_state, st.state_idx, st.has_init, dyk[idx1],
+                             ds2)
+    one = oracle.backward_one(st.k, cu, w.k_taps, w.k_gamma, w.eps, w.k_state, st.state_idx,
+                              st.has_init, oracle.widen(dyk), gs, cond=True)
+    dx = np.zeros_like(one.dx)
+    dx[idx1], dx[idx2] = dx1, dx2
+    _judge("dx", dx, one.dx, one.cond_dx, 1e-5, K_ROWS)
+    _judge("dtaps", dt1 + dt2, one.dtaps, one.cond_dtaps, 1e-5, K_PARAMS)
+    _judge("dgamma", dg1 + dg2, one.dgamma, one.cond_dgamma, 1e-5, K_PARAMS)
+    _judge("dstate", ds1, one.dstate, one.cond_dstate, 1e-5, K_ROWS)
