@@ -610,7 +610,8 @@ def pin_backward_finite_differences():
             an_s[st.state_idx[s]] += gr.dstate[s]
         for name, fd, an in (("dx", fd_x, gr.dx), ("dtaps", fd_t, gr.dtaps),
                              ("dgamma", fd_g, gr.dgamma), ("dstate", fd_s, an_s)):
-            assert np.allclose(an, fd, rtol=1e-6, atol=1e-6), f"{name} != finite differences (W={W})"
+            assert np.allclose(an, fd, rtol=1e-6, atol=1e-6), \
+                f"{name} != finite differences (W={W})"
     # bf16 storage changes nothing but the widening: same values stored as fp32 give the same
     # gradients, bit for bit
     w, st, g, gs = _bwd_case(dtype="bf16")
