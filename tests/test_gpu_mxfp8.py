@@ -269,3 +269,32 @@ def test_mx_graph_replay_matches_eager():
         got = [t.cpu().numpy() for t in (mx2.k_codes, mx2.v_codes, mx2.k_scales, mx2.v_scales)]
         for a, b in zip(got, eager):
             assert np.array_equal(a[rows], b[rows])
+
+
+def test_varlen_workload_mx_rows_at_full_size():
+    """The bench's MXFP8 measurement (the varlen prefill workload with MXFP8 rows) at full size:
+    codes and scales equal the oracle's quantization of the plain kernel's bf16 rows except at
+    the identified double-rounding ties; the conv state equals the plain run's."""
+    w = workloads.config("varlen_prefill")
+    plain, mx = _fused_pair(w)
+    rows = _written_slots(w)
+    mids = oracle.e4m3_decode(np.arange(0, 0x7E))
+    mids = (mids + oracle.e4m3_decode(np.arange(1, 0x7F))) / 2.0
+    for cache, codes_d, scales_d in ((plain.k_cache, mx.k_codes, mx.k_scales),
+                                     (plain.v_cache, mx.v_codes, mx.v_scales)):
+        for a in range(0, rows.size, 4096):
+            sel = rows[a:a + 4096]
+            idx = torch.from_numpy(sel).to(DEV)
+            yb = oracle.widen(to_host(cache.index_select(0, idx), "bf16"))
+            ec, es = oracle.mxfp8_quantize(yb)
+            gc = codes_d.index_select(0, idx).cpu().numpy()
+            gs = scales_d.index_select(0, idx).cpu().numpy()
+            blocks = np.abs(yb).reshape(*yb.shape[:-1], -1, 32).max(-1)
+            pow2 = (blocks > 0) & (np.frexp(blocks)[0] == 0.5)
+            assert (pow2 | (gs == es)).all(), "a scale differs off a power-of-two block maximum"
+            same = np.repeat(gs == es, 32, axis=-1)
+            e = np.repeat(es.astype(np.int64) - 127, 32, axis=-1)
+            tie = np.isin(np.abs(yb) * np.exp2(-e.astype(np.float64)), mids)
+            assert (tie | ~((gc != ec) & same)).all(), "a code differs off an E4M3 midpoint"
+    for a, b in ((plain.k_state, mx.k_state), (plain.v_state, mx.v_state)):
+        assert np.array_equal(to_host(a, "bf16"), to_host(b, "bf16"))

@@ -200,3 +200,27 @@ def test_verify_commit_graph_replay_matches_eager():
             n = min(L, max_tokens)
             for a, b in zip(got[4:], eager[4:]):
                 assert np.array_equal(a[s, :n], b[s, :n]), f"snapshots of sequence {s}"
+
+
+def test_spec_verify_workload_at_full_size():
+    """The bench's speculative step (workloads.spec_verify: 256 sequences x 4 candidate tokens,
+    decode-sized paged pool) at full size: cache rows against the oracle, every snapshot and the
+    committed pools bit for bit."""
+    w, accepted = workloads.spec_verify(0)
+    st = w.steps[0]
+    mt = workloads.SPEC_TOKENS
+    dw, ks, vs = _run_verify(w, mt)
+    r, eks, evs = oracle.fused_verify(st.k, st.v, st.cu_seqlens, w.k_taps, w.v_taps, w.k_gamma,
+                                      w.v_gamma, w.eps, w.k_state, w.v_state, st.state_idx,
+                                      st.slot_mapping, w.num_slots, mt)
+    judge(dw, [r])
+    lens = np.diff(st.cu_seqlens).tolist()
+    _check_snaps(w, ks, eks, lens, mt)
+    _check_snaps(w, vs, evs, lens, mt)
+    d = dw.steps[0]
+    shortconv_state_commit(ks, vs, d["cu"], st.tokens, to_dev(accepted), dw.k_state, dw.v_state,
+                           d["sidx"], width=w.W, num_heads=w.H, head_dim=w.D)
+    torch.cuda.synchronize()
+    for dev, pool, snaps in ((dw.k_state, w.k_state, eks), (dw.v_state, w.v_state, evs)):
+        exp = oracle.commit_state(pool, snaps, accepted, st.cu_seqlens, st.state_idx, mt)
+        assert np.array_equal(to_host(dev, "bf16"), exp)
