@@ -60,15 +60,16 @@ __device__ inline void st16(void* base, int64_t elem_off, int bytes, const uint4
 }
 // Row access as (wave-uniform byte base, per-lane 32-bit byte offset). K/V rows are read once and
 // cache rows are written once, so both stream with the non-temporal hint: they do not displace
-// reusable lines (taps, gamma, halo rows, metadata) from L2 and the Infinity Cache, and dirty cache
-// rows do not linger there (measured on MI355X: a cold 140 MB copy streams at ~5.7 TB/s with the
-// hint against ~3.0 TB/s without).
+// reusable lines (taps, gamma, metadata) from L2 and the Infinity Cache, and dirty cache rows do
+// not linger there (measured on MI355X: a cold 140 MB copy streams at ~5.7 TB/s with the hint
+// against ~3.0 TB/s without).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ inline uint4 ldrow(const char* base, uint32_t lane_off) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + lane_off));
     return make_uint4(v.x, v.y, v.z, v.w);
 }
-// The same load without the streaming hint: the line stays in L2 for a later reader.
+// The same load without the streaming hint. The kernels use it for a few rows of each span (a
+// mix that measured faster than streaming every row; see where it is used).
 __device__ inline uint4 ldrow_keep(const char* base, uint32_t lane_off) {
     return *reinterpret_cast<const uint4*>(base + lane_off);
 }
