@@ -305,3 +305,45 @@ def test_graph_replay_matches_eager():
         rows = np.concatenate([st.slot_mapping for st in w.steps])
         for a, b in zip(got[:2], eager[:2]):
             assert np.array_equal(a[rows], b[rows])
+
+
+def test_null_state_idx_and_has_init_mean_identity_and_all_resumed():
+    """state_idx = NULL means pool row s for sequence s (row b for decode b) and
+    has_initial_state = NULL means every sequence resumes: the results equal those of the
+    explicit arange / all-ones arrays, bit for bit (prefill, decode and the backward)."""
+    from causal_short_convolution_amd import shortconv_kv_backward
+    spec = workloads.Spec(dtype="bf16", H=4, D=128, W=4, seed=23, prefill_lens=[30, 2, 0, 45],
+                          has_init=[1, 1, 1, 1], decode_ctx=[7, 19, 3, 60], block_size=16)
+    w = workloads.build(spec)
+    pre, dec = w.steps
+    N, B = pre.num_seqs, dec.tokens
+    S = w.num_state_slots  # N + B rows; prefill uses rows 0..N-1, decode rows 0..B-1
+    outs = []
+    for explicit in (True, False):
+        kc = torch.zeros((w.num_slots, 4, 128), dtype=torch.bfloat16, device=DEV)
+        vc = torch.zeros_like(kc)
+        ks, vs = to_dev(w.k_state), to_dev(w.v_state)
+        args = (to_dev(w.k_taps), to_dev(w.v_taps), to_dev(w.k_gamma), to_dev(w.v_gamma), w.eps)
+        sidx_p = to_dev(np.arange(N, dtype=np.int32)) if explicit else None
+        hin = to_dev(np.ones(N, np.uint8)) if explicit else None
+        shortconv_kv_prefill(rows_to_dev(pre.k), rows_to_dev(pre.v), to_dev(pre.cu_seqlens),
+                             *args, ks, vs, sidx_p, hin, to_dev(pre.slot_mapping), kc, vc)
+        sidx_d = to_dev(np.arange(B, dtype=np.int32)) if explicit else None
+        shortconv_kv_decode(rows_to_dev(dec.k), rows_to_dev(dec.v), *args, ks, vs, sidx_d,
+                            to_dev(dec.slot_mapping), kc, vc)
+        g = torch.ones((pre.tokens, 4, 128), dtype=torch.bfloat16, device=DEV)
+        dk, dv = torch.empty_like(g), torch.empty_like(g)
+        grads = [torch.empty((4, 4, 128), device=DEV) for _ in range(2)] + \
+                [torch.empty(128, device=DEV) for _ in range(2)]
+        dsk = torch.empty((N, 3, 4, 128), dtype=torch.bfloat16, device=DEV)
+        dsv = torch.empty_like(dsk)
+        shortconv_kv_backward(rows_to_dev(pre.k), rows_to_dev(pre.v), to_dev(pre.cu_seqlens),
+                              *args, to_dev(w.k_state), to_dev(w.v_state), sidx_p, hin, g, g,
+                              dk, dv, *grads, dstate_in=(dsk, dsv))
+        torch.cuda.synchronize()
+        outs.append([to_host(t, "bf16") for t in (kc, vc, ks, vs, dk, dv, dsk, dsv)] +
+                    [t.cpu().numpy() for t in grads])
+    assert S >= max(N, B)
+    for i, (a, b) in enumerate(zip(*outs)):
+        assert np.array_equal(np.ascontiguousarray(a).view(np.uint8),
+                              np.ascontiguousarray(b).view(np.uint8)), f"output {i}"
