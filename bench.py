@@ -461,6 +461,70 @@ def cpu_baseline(w, budget_s):
                       f"{time.process_time() - c0:.1f} s CPU on {threads} threads"}
 
 
+def _timed(fn, budget_s):
+    """Run fn repeatedly for about budget_s seconds of CPU time; (repetitions, wall, cpu)."""
+    reps = 0
+    c0, t0 = time.process_time(), time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        if time.process_time() - c0 >= budget_s:
+            break
+    return reps, time.perf_counter() - t0, time.process_time() - c0
+
+
+def cpu_baseline_extras(w, budget_s):
+    """The oracle beside the extra measurements, each on the same workload as its GPU figure and
+    about budget_s seconds of CPU: the MXFP8 rows of workload w's prefill (the step plus the
+    quantizer), the speculative verify + commit step, and the backward of w's prefill."""
+    import numpy as np
+    import oracle
+    import workloads
+    threads = max(1, min(16, os.cpu_count() or 1))
+    out = {}
+    st = w.steps[0]
+
+    def mx():
+        r = oracle.fused_prefill(st.k, st.v, st.cu_seqlens, w.k_taps, w.v_taps, w.k_gamma,
+                                 w.v_gamma, w.eps, w.k_state, w.v_state, st.state_idx,
+                                 st.has_init, st.slot_mapping, w.num_slots, cond=False,
+                                 nthreads=threads)
+        oracle.mxfp8_quantize(r.y_k)
+        oracle.mxfp8_quantize(r.y_v)
+    n, wall, cpu = _timed(mx, budget_s)
+    out["mxfp8_cache"] = {"value": st.tokens * n / wall, "unit": "tokens/s",
+                          "sample": f"{w.name} prefill + MXFP8 encoding x{n}: {wall:.1f} s wall, "
+                                    f"{cpu:.1f} s CPU"}
+    wv, acc = workloads.spec_verify(0)
+    sv = wv.steps[0]
+
+    def verify():
+        _, ks, vs = oracle.fused_verify(sv.k, sv.v, sv.cu_seqlens, wv.k_taps, wv.v_taps,
+                                        wv.k_gamma, wv.v_gamma, wv.eps, wv.k_state, wv.v_state,
+                                        sv.state_idx, sv.slot_mapping, wv.num_slots,
+                                        workloads.SPEC_TOKENS, cond=False, nthreads=threads)
+        oracle.commit_state(wv.k_state, ks, acc, sv.cu_seqlens, sv.state_idx,
+                            workloads.SPEC_TOKENS)
+        oracle.commit_state(wv.v_state, vs, acc, sv.cu_seqlens, sv.state_idx,
+                            workloads.SPEC_TOKENS)
+    n, wall, cpu = _timed(verify, budget_s)
+    out["spec_verify"] = {"value": sv.tokens * n / wall, "unit": "tokens/s",
+                          "sample": f"spec_verify (verify + commit) x{n}: {wall:.1f} s wall, "
+                                    f"{cpu:.1f} s CPU"}
+    if all(x.kind == "prefill" for x in w.steps):
+        g = np.random.default_rng(0).standard_normal((st.tokens, w.H, w.D))
+
+        def bwd():
+            oracle.fused_backward(st.k, st.v, st.cu_seqlens, w.k_taps, w.v_taps, w.k_gamma,
+                                  w.v_gamma, w.eps, w.k_state, w.v_state, st.state_idx,
+                                  st.has_init, g, g, nthreads=threads)
+        n, wall, cpu = _timed(bwd, budget_s)
+        out["backward"] = {"value": st.tokens * n / wall, "unit": "tokens/s",
+                           "sample": f"{w.name} backward x{n}: {wall:.1f} s wall, "
+                                     f"{cpu:.1f} s CPU"}
+    return out
+
+
 # ------------------------------------------------------------------------------------------------
 # Profile summaries (rocprofv3 CSV output -> a short text summary for profiles/)
 # ------------------------------------------------------------------------------------------------
@@ -642,6 +706,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        if not args.no_extras:
+            line["cpu_baseline"]["extras"] = cpu_baseline_extras(w, args.cpu_seconds / 3)
     print(json.dumps(line), flush=True)
     return 0
 
