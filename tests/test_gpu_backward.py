@@ -311,3 +311,13 @@ def test_chunked_backward_composes_to_oneshot(W):
     _judge("dtaps", dt1 + dt2, one.dtaps, one.cond_dtaps, 1e-5, K_PARAMS)
     _judge("dgamma", dg1 + dg2, one.dgamma, one.cond_dgamma, 1e-5, K_PARAMS)
     _judge("dstate", ds1, one.dstate, one.cond_dstate, 1e-5, K_ROWS)
+
+
+def test_backward_five_thousand_sequences():
+    """The backward over 5 000 short packed sequences (a three-round tile search)."""
+    g = np.random.default_rng(19)
+    n = 5000
+    lens = g.integers(0, 5, size=n).tolist()
+    hin = (g.random(n) < 0.5).astype(int).tolist()
+    case = BwdCase("bf16", 2, 64, 4, lens, hin, seed=20)
+    case.check()

@@ -347,3 +347,14 @@ def test_null_state_idx_and_has_init_mean_identity_and_all_resumed():
     for i, (a, b) in enumerate(zip(*outs)):
         assert np.array_equal(np.ascontiguousarray(a).view(np.uint8),
                               np.ascontiguousarray(b).view(np.uint8)), f"output {i}"
+
+
+def test_five_thousand_sequences():
+    """5 000 packed sequences (0 to 4 tokens each): the tile search narrows 64-fold per round, so
+    this takes three rounds; every cache row and the whole state pool against the oracle."""
+    g = np.random.default_rng(17)
+    n = 5000
+    lens = g.integers(0, 5, size=n).tolist()
+    spec = workloads.Spec(dtype="bf16", H=2, D=64, W=4, seed=18, prefill_lens=lens,
+                          has_init=(g.random(n) < 0.5).astype(int).tolist(), block_size=16)
+    _run_and_judge(workloads.build(spec))
