@@ -2,7 +2,7 @@
 """Benchmark of the fused ShortConv K/V step on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload varlen_prefill] [--no-cpu-baseline]
-                    [--no-decode] [--no-extras] [--only main|decode|mxfp8|verify|backward]
+                    [--no-decode] [--no-extras] [--only main|decode|mxfp8|verify|backward|copy]
 
 A step is one call of the fused step over one batch of the workload (for the default workload:
 8 packed sequences of U{512..4096} tokens, 8 KV heads x 128, W = 4, bf16 rows with fp32
@@ -17,12 +17,15 @@ Prints ONE JSON line: tokens/s over the timed steps (wall clock between two devi
 synchronizations), the average duration of one step (device time between HIP events recorded on
 the launch stream before the first and after the last launch, divided by K), algorithmic HBM
 bytes / that duration against the 8 TB/s peak (`roofline`, with the counter-measured `traffic`
-while profiles/ holds counters for these kernel sources), a same-bytes copy (`copy_ceiling`), the
-same measurement for the decode step (256 sequences x 1 token), the workload with MXFP8 cache
-rows, a speculative verify + commit step and the backward of the prefill, and the fp64 CPU
-oracle timed on host cores (`cpu_baseline`). --only NAME runs one measurement and prints a
-line of text instead (for profiling and sweeps); --workload picks another of the five
-configurations.
+while profiles/ holds counters for these kernel sources), a same-bytes copy (`copy_ceiling`), and
+the fp64 CPU oracle timed on the host's cores and on one core (`cpu_baseline`). Beside the
+headline workload the line carries the same measurement for each of the other four workloads
+(`tiny_ref`, `decode`, `long_prefill`, `mixed`: time, algorithmic bytes, fraction of 8 TB/s,
+same-bytes copy ceiling, the oracle on the host), for the two large ones also with MXFP8 cache
+rows and the backward of their prefill call, and for the headline workload the MXFP8 rows, a
+speculative verify + commit step and the backward. --no-extras keeps the headline only.
+--only NAME runs one measurement and prints a line of text instead (for profiling and sweeps);
+--workload picks another of the five workloads as the headline.
 
 Profiling helpers (run under rocprofv3, then summarize):
     --calibrate-copy         also run a plain device copy of known size (counter calibration)
@@ -136,9 +139,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the MXFP8-cache, speculative-verify and backward measurements")
+                    help="measure the headline workload only (no other workloads, MXFP8 rows, "
+                         "speculative verify or backward)")
     ap.add_argument("--only", default=None,
-                    choices=["main", "decode", "mxfp8", "verify", "backward"],
+                    choices=["main", "decode", "mxfp8", "verify", "backward", "copy"],
                     help="run one measurement only (for profiling); prints no JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -156,7 +160,7 @@ def device_replicas(w, torch, n_rep, reseed=None, cache="io"):
     """n_rep device copies of workload w (fresh buffers each). With reseed, replica r > 0 is
     drawn again with another seed (reseed(r)), so its slots differ and writes never revisit a
     row, and all replicas share one cache pool (decode-style pools are tens of GB). cache="io"
-    allocates I/O-dtype cache rows, "mxfp8" code and scale rows."""
+    allocates I/O-dtype cache rows, "mxfp8" code and scale rows, None no cache at all."""
     import numpy as np
     from causal_short_convolution_amd import _binding  # noqa: F401  (fails loudly if not built)
 
@@ -198,7 +202,9 @@ def device_replicas(w, torch, n_rep, reseed=None, cache="io"):
                 "k_scales": torch.empty((ns, w.H, w.D // 32), dtype=u8, device=dev),
                 "v_scales": torch.empty((ns, w.H, w.D // 32), dtype=u8, device=dev)}
 
-    if reseed is not None:  # one pool large enough for every replica's slots
+    if cache is None:
+        pass
+    elif reseed is not None:  # one pool large enough for every replica's slots
         shared_pool = pool(max(r["num_slots"] for r in reps))
         for r in reps:
             r.update(shared_pool)
@@ -288,10 +294,18 @@ def time_steps(torch, fns, steps, warmup, graph=True):
     return wall, start.elapsed_time(end)
 
 
+def replica_count(step_bytes):
+    """Distinct input copies so that a step never finds its data in the Infinity Cache: enough
+    that 2x its capacity passes between two uses of a copy; one when a step alone moves 4x it."""
+    if step_bytes >= 4 * MALL_BYTES:
+        return 1
+    return max(2, math.ceil(2 * MALL_BYTES / step_bytes) + 1)
+
+
 def measure(torch, w, steps, warmup, reseed=None, graph=True, cache="io"):
     alg = sum(algorithmic_bytes(w, st, cache) for st in w.steps)
     tokens = w.tokens
-    n_rep = max(2, math.ceil(2 * MALL_BYTES / alg) + 1)
+    n_rep = replica_count(alg)
     reps = device_replicas(w, torch, n_rep, reseed, cache)
     fns = [launcher(w, r, cache) for r in reps]
     wall, dev_ms = time_steps(torch, fns, steps, warmup, graph)
@@ -318,7 +332,7 @@ def measure_verify(torch, steps, warmup, seed, graph=True):
     w, accepted = workloads.spec_verify(seed)
     mt = workloads.SPEC_TOKENS
     vb, cb = verify_bytes(w, accepted, mt)
-    n_rep = max(2, math.ceil(2 * MALL_BYTES / (vb + cb)) + 1)
+    n_rep = replica_count(vb + cb)
     draws = {0: (w, accepted)}
 
     def reseed(r):
@@ -352,15 +366,15 @@ def backward_bytes(w):
 
 
 def measure_backward(torch, w, steps, warmup, graph=True):
-    """One backward call (shortconv_kv_backward) over the prefill of workload w, with random
-    output gradients; no new-state loss, no initial-state gradient (a fresh training batch)."""
+    """One backward call (shortconv_kv_backward) over the prefill call of workload w (its first
+    call), with random output gradients; no new-state loss, no initial-state gradient."""
     import numpy as np
     import causal_short_convolution_amd as sc
     st = w.steps[0]
     dev = "cuda:0"
     alg = backward_bytes(w)
-    n_rep = max(2, math.ceil(2 * MALL_BYTES / alg) + 1)
-    reps = device_replicas(w, torch, n_rep)
+    n_rep = replica_count(alg)
+    reps = device_replicas(w, torch, n_rep, cache=None)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     T, H, D, W = st.tokens, w.H, w.D, w.W
     ws = torch.empty(max(16, sc.shortconv_kv_backward_workspace_size(T, st.num_seqs, H, D, W, dt)),
@@ -384,7 +398,7 @@ def measure_backward(torch, w, steps, warmup, graph=True):
     wall, dev_ms = time_steps(torch, fns, steps, warmup, graph)
     del reps, fns
     per_ms = dev_ms / steps
-    return {"workload": w.name, "tokens_per_step": T, "launches_per_step": 2, "replicas": n_rep,
+    return {"workload": w.name, "tokens_per_step": T, "launches_per_step": 3, "replicas": n_rep,
             "ms_per_step": 1e3 * wall / steps, "tokens_per_s": T * steps / wall,
             "kernel_us_mean": 1e3 * per_ms, "algorithmic_bytes": alg,
             "workspace_bytes": ws.numel(), "achieved_GBps": alg / (per_ms * 1e-3) / 1e9}
@@ -400,7 +414,7 @@ def copy_ceiling(torch, bytes_moved, steps, warmup):
     lib.sc_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                   ctypes.c_void_p]
     half = (bytes_moved // 2) // 16 * 16
-    n_rep = max(2, math.ceil(2 * MALL_BYTES / (2 * half)) + 1)
+    n_rep = replica_count(2 * half)
     bufs = [(torch.empty(half, dtype=torch.uint8, device="cuda:0"),
              torch.empty(half, dtype=torch.uint8, device="cuda:0")) for _ in range(n_rep)]
 
@@ -430,35 +444,17 @@ def calibration_copy(torch):
 # ------------------------------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle, as it stands, on the same workload
 # ------------------------------------------------------------------------------------------------
-def cpu_baseline(w, budget_s):
-    """The oracle on the whole workload (every call, the state pools carried from call to call),
-    repeated until about budget_s seconds of CPU time have been spent."""
-    import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
-    reps = 0
-    c0, t0 = time.process_time(), time.perf_counter()
-    while True:
-        ks, vs = w.k_state, w.v_state
-        for st in w.steps:
-            if st.kind == "prefill":
-                r = oracle.fused_prefill(st.k, st.v, st.cu_seqlens, w.k_taps, w.v_taps, w.k_gamma,
-                                         w.v_gamma, w.eps, ks, vs, st.state_idx, st.has_init,
-                                         st.slot_mapping, w.num_slots, cond=False,
-                                         nthreads=threads)
-            else:
-                r = oracle.fused_decode(st.k, st.v, w.k_taps, w.v_taps, w.k_gamma, w.v_gamma,
-                                        w.eps, ks, vs, st.state_idx, st.slot_mapping,
-                                        w.num_slots, cond=False, nthreads=threads)
-            ks, vs = r.k_state, r.v_state
-        reps += 1
-        if time.process_time() - c0 >= budget_s:
-            break
-    wall = time.perf_counter() - t0
-    return {"value": w.tokens * reps / wall, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"the whole {w.name} workload ({w.tokens} tokens, K and V, fp64) "
-                      f"repeated {reps}x: {wall:.1f} s wall, "
-                      f"{time.process_time() - c0:.1f} s CPU on {threads} threads"}
+def host_cores():
+    """(threads the oracle runs on, CPUs this process may use). The first is the host's CPU share
+    for this GPU: OMP_NUM_THREADS when the environment sets it (shared GPU hosts give each GPU a
+    fixed share of their cores), else every CPU in this process's affinity set."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # not Linux
+        avail = os.cpu_count() or 1
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(avail, int(share)) if share.isdigit() and int(share) > 0 else avail
+    return max(1, threads), avail
 
 
 def _timed(fn, budget_s):
@@ -473,14 +469,53 @@ def _timed(fn, budget_s):
     return reps, time.perf_counter() - t0, time.process_time() - c0
 
 
+def oracle_step_fn(w, threads):
+    """The oracle on every call of workload w, the state pools carried from call to call."""
+    import oracle
+
+    def run():
+        ks, vs = w.k_state, w.v_state
+        for st in w.steps:
+            if st.kind == "prefill":
+                r = oracle.fused_prefill(st.k, st.v, st.cu_seqlens, w.k_taps, w.v_taps, w.k_gamma,
+                                         w.v_gamma, w.eps, ks, vs, st.state_idx, st.has_init,
+                                         st.slot_mapping, w.num_slots, cond=False,
+                                         nthreads=threads)
+            else:
+                r = oracle.fused_decode(st.k, st.v, w.k_taps, w.v_taps, w.k_gamma, w.v_gamma,
+                                        w.eps, ks, vs, st.state_idx, st.slot_mapping,
+                                        w.num_slots, cond=False, nthreads=threads)
+            ks, vs = r.k_state, r.v_state
+    return run
+
+
+def cpu_baseline(w, budget_s, one_core_s):
+    """The oracle on the whole workload w (every call, fp64), repeated for about budget_s seconds
+    of CPU time on the host's cores, and for about one_core_s seconds on one thread."""
+    threads, avail = host_cores()
+    n, wall, cpu = _timed(oracle_step_fn(w, threads), budget_s)
+    out = {"value": w.tokens * n / wall, "unit": "tokens/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"the whole {w.name} workload ({w.tokens} tokens, K and V, fp64) "
+                     f"repeated {n}x: {wall:.1f} s wall, {cpu:.1f} s CPU on {threads} threads",
+           "nproc": avail}
+    if one_core_s > 0:
+        n1, wall1, cpu1 = _timed(oracle_step_fn(w, 1), one_core_s)
+        out["one_core"] = {"value": w.tokens * n1 / wall1, "unit": "tokens/s", "cores": 1,
+                           "sample": f"the same workload repeated {n1}x on one thread: "
+                                     f"{wall1:.1f} s wall"}
+    return out
+
+
 def cpu_baseline_extras(w, budget_s):
-    """The oracle beside the extra measurements, each on the same workload as its GPU figure and
-    about budget_s seconds of CPU: the MXFP8 rows of workload w's prefill (the step plus the
-    quantizer), the speculative verify + commit step, and the backward of w's prefill."""
+    """The oracle beside the extra measurements of workload w (a prefill workload), each on the
+    same workload as its GPU figure and about budget_s seconds of CPU on the host's cores: the
+    MXFP8 rows of w's prefill (the step plus the quantizer), the speculative verify + commit step
+    and the backward of w's prefill."""
     import numpy as np
     import oracle
     import workloads
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads, _ = host_cores()
     out = {}
     st = w.steps[0]
 
@@ -492,7 +527,7 @@ def cpu_baseline_extras(w, budget_s):
         oracle.mxfp8_quantize(r.y_k)
         oracle.mxfp8_quantize(r.y_v)
     n, wall, cpu = _timed(mx, budget_s)
-    out["mxfp8_cache"] = {"value": st.tokens * n / wall, "unit": "tokens/s",
+    out["mxfp8_cache"] = {"value": st.tokens * n / wall, "unit": "tokens/s", "cores": threads,
                           "sample": f"{w.name} prefill + MXFP8 encoding x{n}: {wall:.1f} s wall, "
                                     f"{cpu:.1f} s CPU"}
     wv, acc = workloads.spec_verify(0)
@@ -508,21 +543,28 @@ def cpu_baseline_extras(w, budget_s):
         oracle.commit_state(wv.v_state, vs, acc, sv.cu_seqlens, sv.state_idx,
                             workloads.SPEC_TOKENS)
     n, wall, cpu = _timed(verify, budget_s)
-    out["spec_verify"] = {"value": sv.tokens * n / wall, "unit": "tokens/s",
+    out["spec_verify"] = {"value": sv.tokens * n / wall, "unit": "tokens/s", "cores": threads,
                           "sample": f"spec_verify (verify + commit) x{n}: {wall:.1f} s wall, "
                                     f"{cpu:.1f} s CPU"}
-    if all(x.kind == "prefill" for x in w.steps):
-        g = np.random.default_rng(0).standard_normal((st.tokens, w.H, w.D))
-
-        def bwd():
-            oracle.fused_backward(st.k, st.v, st.cu_seqlens, w.k_taps, w.v_taps, w.k_gamma,
-                                  w.v_gamma, w.eps, w.k_state, w.v_state, st.state_idx,
-                                  st.has_init, g, g, nthreads=threads)
-        n, wall, cpu = _timed(bwd, budget_s)
-        out["backward"] = {"value": st.tokens * n / wall, "unit": "tokens/s",
-                           "sample": f"{w.name} backward x{n}: {wall:.1f} s wall, "
-                                     f"{cpu:.1f} s CPU"}
+    out["backward"] = cpu_baseline_backward(w, budget_s)
     return out
+
+
+def cpu_baseline_backward(w, budget_s):
+    """The oracle's backward of workload w's prefill call, about budget_s seconds of CPU."""
+    import numpy as np
+    import oracle
+    threads, _ = host_cores()
+    st = w.steps[0]
+    g = np.random.default_rng(0).standard_normal((st.tokens, w.H, w.D))
+
+    def bwd():
+        oracle.fused_backward(st.k, st.v, st.cu_seqlens, w.k_taps, w.v_taps, w.k_gamma,
+                              w.v_gamma, w.eps, w.k_state, w.v_state, st.state_idx,
+                              st.has_init, g, g, nthreads=threads)
+    n, wall, cpu = _timed(bwd, budget_s)
+    return {"value": st.tokens * n / wall, "unit": "tokens/s", "cores": threads,
+            "sample": f"{w.name} backward x{n}: {wall:.1f} s wall, {cpu:.1f} s CPU"}
 
 
 # ------------------------------------------------------------------------------------------------
@@ -591,6 +633,32 @@ def summarize_profile(dirs):
 
 
 # ------------------------------------------------------------------------------------------------
+def config_measure(torch, name, args, graph, cache="io"):
+    """The fused step on workload `name` (every call of one step, in order), with the same-bytes
+    copy ceiling. Returns (workload, entry)."""
+    import workloads
+    w = workloads.config(name, seed=args.seed)
+    has_decode = any(st.kind == "decode" for st in w.steps)
+    reseed = ((lambda r: workloads.config(name, seed=args.seed + 1000 * r))
+              if has_decode else None)
+    m = measure(torch, w, args.steps, args.warmup, reseed, graph, cache)
+    entry = {"workload": w.name, "recipe": w.recipe, **_round(m),
+             "kernels": "+".join(f"{x.kind}_kernel" for x in w.steps),
+             "frac_of_hbm_peak": m["achieved_GBps"] / HBM_PEAK_GBPS}
+    if cache == "io":
+        c = copy_ceiling(torch, m["algorithmic_bytes"], args.steps, args.warmup)
+        entry["copy_ceiling_GBps"] = c["GBps"]
+        entry["kernel_over_copy"] = m["achieved_GBps"] / c["GBps"]
+    return w, entry
+
+
+def free_device(torch):
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.summarize_profile:
@@ -628,38 +696,70 @@ def main():
                         lambda r: workloads.config("decode", seed=args.seed + 1000 * r), graph)
         elif args.only == "backward":
             m = measure_backward(torch, w, args.steps, args.warmup, graph)
+        elif args.only == "copy":
+            m = measure(torch, w, 1, 0, reseed_main, graph)
+            m = copy_ceiling(torch, m["algorithmic_bytes"], args.steps, args.warmup)
+            m["achieved_GBps"] = m["GBps"]
         else:
             m = measure_verify(torch, args.steps, args.warmup, args.seed, graph)
         print(f"bench.py: {args.only}: {m['kernel_us_mean']:.2f} us per step, "
               f"{m['achieved_GBps']:.0f} GB/s", flush=True)
         return 0
+
+    def progress(what):
+        print(f"bench.py: {what}", file=sys.stderr, flush=True)
+
+    progress(f"{n}: fused step")
     main_m = measure(torch, w, args.steps, args.warmup, reseed_main, graph)
     extra = {}
-    if not args.no_decode and args.workload != "decode":
-        wd = workloads.config("decode", seed=args.seed)
-        dm = measure(torch, wd, args.steps, args.warmup,
-                     reseed=lambda r: workloads.config("decode", seed=args.seed + 1000 * r),
-                     graph=graph)
-        dceil = copy_ceiling(torch, dm["algorithmic_bytes"], args.steps, args.warmup)
-        extra["decode"] = {"workload": "decode", "recipe": wd.recipe, **_round(dm),
-                           "frac_of_hbm_peak": dm["achieved_GBps"] / HBM_PEAK_GBPS,
-                           "copy_ceiling_GBps": dceil["GBps"],
-                           "kernel_over_copy": dm["achieved_GBps"] / dceil["GBps"]}
+    others = [] if args.no_extras else [c for c in workloads.CONFIG_NAMES if c != n]
+    if args.no_decode and "decode" in others:
+        others.remove("decode")
+    big = ("long_prefill", "mixed")
+    for name in others:
+        progress(f"{name}: fused step")
+        wc, entry = config_measure(torch, name, args, graph)
+        free_device(torch)
+        if name in big:
+            progress(f"{name}: MXFP8 cache rows")
+            _, mx = config_measure(torch, name, args, graph, cache="mxfp8")
+            free_device(torch)
+            entry["mxfp8_cache"] = {k: mx[k] for k in ("kernel_us_mean", "algorithmic_bytes",
+                                                       "achieved_GBps", "frac_of_hbm_peak",
+                                                       "tokens_per_s")}
+            progress(f"{name}: backward of the prefill call")
+            bm = measure_backward(torch, wc, args.steps, args.warmup, graph)
+            free_device(torch)
+            entry["backward"] = {**_round(bm),
+                                 "frac_of_hbm_peak": bm["achieved_GBps"] / HBM_PEAK_GBPS}
+        if not args.no_cpu_baseline:
+            progress(f"{name}: oracle on the host")
+            cb = cpu_baseline(wc, args.cpu_seconds / 3, 0)
+            cb.pop("nproc")
+            entry["cpu_baseline"] = cb
+            if name in big:
+                entry["cpu_baseline"]["backward"] = cpu_baseline_backward(wc, args.cpu_seconds / 3)
+        extra[name] = entry
+        del wc
     if not args.no_extras:
+        progress(f"{n}: MXFP8 cache rows")
         mm = measure(torch, w, args.steps, args.warmup, reseed_main, graph, cache="mxfp8")
         extra["mxfp8_cache"] = {"workload": w.name, **_round(mm),
                                 "frac_of_hbm_peak": mm["achieved_GBps"] / HBM_PEAK_GBPS,
                                 "vs_io_cache_time": mm["kernel_us_mean"] /
                                 main_m["kernel_us_mean"]}
+        progress("spec_verify: verify + commit")
         vm = measure_verify(torch, args.steps, args.warmup, args.seed, graph)
         extra["spec_verify"] = {**_round(vm),
                                 "frac_of_hbm_peak": vm["achieved_GBps"] / HBM_PEAK_GBPS}
-        if all(st.kind == "prefill" for st in w.steps):
-            bm = measure_backward(torch, w, args.steps, args.warmup, graph)
-            extra["backward"] = {**_round(bm),
-                                 "frac_of_hbm_peak": bm["achieved_GBps"] / HBM_PEAK_GBPS}
+        progress(f"{n}: backward")
+        bm = measure_backward(torch, w, args.steps, args.warmup, graph)
+        extra["backward"] = {**_round(bm),
+                             "frac_of_hbm_peak": bm["achieved_GBps"] / HBM_PEAK_GBPS}
+        free_device(torch)
     if args.calibrate_copy:
         calibration_copy(torch)
+    progress(f"{n}: same-bytes copy")
     ceil = copy_ceiling(torch, main_m["algorithmic_bytes"], args.steps, args.warmup)
 
     traffic = None
@@ -682,14 +782,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
+        # the arithmetic type of the step (rows are stored as config.io and widened exactly)
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "recipe": w.recipe, "seed": args.seed,
                    "tokens_per_step": w.tokens, "launches_per_step": len(w.steps),
                    "seqs": sum(x.num_seqs for x in w.steps), "heads": w.H,
-                   "head_dim": w.D, "width": w.W, "io": w.dtype, "block_size": w.block_size,
-                   "replicas": main_m["replicas"], "input_sha256": input_digest(w),
-                   "parallelism": "single GPU"},
+                   "head_dim": w.D, "width": w.W, "io": w.dtype, "arithmetic": "f32",
+                   "block_size": w.block_size, "replicas": main_m["replicas"],
+                   "input_sha256": input_digest(w), "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": main_m["achieved_GBps"], "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": main_m["achieved_GBps"] / HBM_PEAK_GBPS,
                      "traffic": traffic,
@@ -705,7 +806,8 @@ def main():
         **extra,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        progress(f"{n}: oracle on the host")
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.cpu_seconds / 3)
         if not args.no_extras:
             line["cpu_baseline"]["extras"] = cpu_baseline_extras(w, args.cpu_seconds / 3)
     print(json.dumps(line), flush=True)
