@@ -73,7 +73,9 @@ enum {
  *                      The kernel clamps every entry into [0, total_tokens].
  *  k_taps, v_taps      fp32 [W][H][D];  k_gamma, v_gamma fp32 [D];  eps >= 0 (e.g. 1e-6).
  *  k_state, v_state    [num_state_slots][W-1][H][D], read and rewritten in place. May be NULL
- *                      only when width == 1 (then num_state_slots is ignored).
+ *                      when width == 1 (num_state_slots is then ignored) or when
+ *                      num_state_slots == 0 (no sequence has a state row: every window starts
+ *                      from zeros and no state is written back).
  *  state_idx           int32 [num_seqs]: pool row of sequence s, or NULL for row s. Entries must
  *                      be distinct. An entry outside [0, num_state_slots) means the sequence has no
  *                      state row: its window starts from zeros and nothing is written back.
@@ -104,8 +106,8 @@ int shortconv_kv_prefill(const void* k, const void* v, int64_t k_tok_stride, int
  *  k_new, v_new        [batch][H][D] (token strides in elements).
  *  k_state, v_state    [num_state_slots][W-1][H][D]; sequence b reads rows 0..W-2 of
  *                      pool row state_idx[b] as the past of its window and then shifts the pool
- *                      row by one (rows 1..W-2 move up, the new raw row goes last). NULL only when
- *                      width == 1.
+ *                      row by one (rows 1..W-2 move up, the new raw row goes last). May be NULL
+ *                      when width == 1 or num_state_slots == 0 (zeros as the past, no write-back).
  *  state_idx           int32 [batch], or NULL for row b. Distinct. Out-of-pool entries: zeros as
  *                      the past, no write-back.
  *  slot_mapping        int64 [batch]: cache row of each new token (outside [0, num_slots) = skip).

@@ -139,10 +139,13 @@ def test_rejects_bad_arguments_without_launch():
     dw = DeviceWorkload(w)
     d = dw.steps[0]
     with pytest.raises(ShortConvError, match="SC_ERR_UNSUPPORTED"):
+        # width 9, with taps and state pools shaped for it (the binding's shape checks pass and
+        # the library's own width check rejects the call)
         bad_taps = torch.zeros((9, 1, 64), dtype=torch.float32, device=DEV)
+        bad_state = torch.zeros((dw.k_state.shape[0], 8, 1, 64), dtype=torch.float32, device=DEV)
         shortconv_kv_prefill(d["k"], d["v"], d["cu"], bad_taps, bad_taps, dw.k_gamma, dw.v_gamma,
-                             w.eps, dw.k_state, dw.v_state, d["sidx"], d["hinit"], d["slot"],
-                             dw.k_cache, dw.v_cache)
+                             w.eps, bad_state, bad_state.clone(), d["sidx"], d["hinit"],
+                             d["slot"], dw.k_cache, dw.v_cache)
     torch.cuda.synchronize()
     judge(dw, results=[oracle.StepResult(*(np.zeros((0, 1, 64)),) * 4, np.zeros(0, np.int64),
                                          w.k_state, w.v_state)])
