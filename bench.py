@@ -704,6 +704,8 @@ def main():
             m = measure_verify(torch, args.steps, args.warmup, args.seed, graph)
         print(f"bench.py: {args.only}: {m['kernel_us_mean']:.2f} us per step, "
               f"{m['achieved_GBps']:.0f} GB/s", flush=True)
+        if args.calibrate_copy:
+            calibration_copy(torch)
         return 0
 
     def progress(what):
