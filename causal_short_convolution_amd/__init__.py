@@ -8,7 +8,8 @@ training (``shortconv_kv``: the step as a differentiable torch op). The compute 
 ``libshortconv.so`` (C ABI, ``include/shortconv.h``); this package only marshals torch tensors.
 """
 from ._binding import (LIBRARY_PATH, ShortConvError, abi_version, last_error, load_library,
-                       shortconv_kv_backward, shortconv_kv_backward_workspace_size,
+                       NOALLOC_SCRATCH_BYTES, shortconv_kv_backward,
+                       shortconv_kv_backward_noalloc, shortconv_kv_backward_workspace_size,
                        shortconv_kv_decode, shortconv_kv_decode_mxfp8, shortconv_kv_prefill,
                        shortconv_kv_prefill_mxfp8, shortconv_kv_verify, shortconv_mxfp8_quantize,
                        shortconv_state_commit)
@@ -21,7 +22,9 @@ __all__ = [
     "abi_version",
     "last_error",
     "load_library",
+    "NOALLOC_SCRATCH_BYTES",
     "shortconv_kv_backward",
+    "shortconv_kv_backward_noalloc",
     "shortconv_kv_backward_workspace_size",
     "shortconv_kv_decode",
     "shortconv_kv_decode_mxfp8",

@@ -65,6 +65,10 @@ def load_library(path: str = LIBRARY_PATH):
     lib.shortconv_kv_backward.argtypes = [P, P, I64, I64, P, I32, I64, P, P, P, P, F, P, P, I64,
                                           P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                           ctypes.c_size_t, I32, I32, I32, I32, P]
+    lib.shortconv_kv_backward_noalloc.restype = ctypes.c_int
+    lib.shortconv_kv_backward_noalloc.argtypes = [P, P, I64, I64, P, I32, I64, P, P, P, P, F, P, P,
+                                                  I64, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                                  I32, I32, I32, I32, P]
     lib.shortconv_kv_backward_workspace_size.restype = ctypes.c_size_t
     lib.shortconv_kv_backward_workspace_size.argtypes = [I64, I32, I32, I32, I32, I32]
     lib.shortconv_last_error.restype = ctypes.c_char_p
@@ -467,4 +471,34 @@ def shortconv_kv_backward(k, v, cu_seqlens, k_taps, v_taps, k_gamma, v_gamma, ep
             _ptr(dv_taps), _ptr(dk_gamma), _ptr(dv_gamma), _ptr(dstate_in[0]), _ptr(dstate_in[1]),
             _ptr(workspace), workspace.numel(), H, D, W, SC_DTYPE[k.dtype],
             _stream_handle(k.device, stream))
+    _check(rc)
+
+
+# The size of the static device scratch of shortconv_kv_backward_noalloc (SHORTCONV_NOALLOC_SCRATCH_BYTES
+# in include/shortconv.h).
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def shortconv_kv_backward_noalloc(k, v, cu_seqlens, k_taps, v_taps, k_gamma, v_gamma, eps,
+                                  k_state, v_state, state_idx, has_initial_state, dy_k, dy_v, dk,
+                                  dv, dk_taps, dv_taps, dk_gamma, dv_gamma, *,
+                                  dstate_out=(None, None), dstate_in=(None, None),
+                                  stream: Optional[torch.cuda.Stream] = None) -> None:
+    """shortconv_kv_backward without a workspace argument and without any allocation: the library
+    uses its static per-GPU scratch (see include/shortconv.h), so problems whose workspace exceeds
+    NOALLOC_SCRATCH_BYTES are rejected, and calls that may overlap on one GPU must be ordered."""
+    a, W, H, D, ks, vs, S, N, T = _backward_args(
+        "shortconv_kv_backward_noalloc", k, v, cu_seqlens, k_taps, v_taps, k_gamma, v_gamma,
+        k_state, v_state, state_idx, has_initial_state, dy_k, dy_v, dk, dv, dk_taps, dv_taps,
+        dk_gamma, dv_gamma, dstate_out, dstate_in)
+    a.on_gpu()
+    lib = load_library()
+    with torch.cuda.device(k.device):
+        rc = lib.shortconv_kv_backward_noalloc(
+            _ptr(k), _ptr(v), ks, vs, _ptr(cu_seqlens), N, T, _ptr(k_taps), _ptr(v_taps),
+            _ptr(k_gamma), _ptr(v_gamma), float(eps), _ptr(k_state), _ptr(v_state), S,
+            _ptr(state_idx), _ptr(_flags(has_initial_state)), _ptr(dy_k), _ptr(dy_v),
+            _ptr(dstate_out[0]), _ptr(dstate_out[1]), _ptr(dk), _ptr(dv), _ptr(dk_taps),
+            _ptr(dv_taps), _ptr(dk_gamma), _ptr(dv_gamma), _ptr(dstate_in[0]), _ptr(dstate_in[1]),
+            H, D, W, SC_DTYPE[k.dtype], _stream_handle(k.device, stream))
     _check(rc)

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "shortconv.h"
 #include "shortconv_internal.h"
 
@@ -392,8 +394,10 @@ SC_API size_t shortconv_kv_backward_workspace_size(int64_t total_tokens, int32_t
         .workspace_bytes;
 }
 
-SC_API int shortconv_kv_backward(
-    const void* k, const void* v, int64_t k_tok_stride, int64_t v_tok_stride,
+namespace {
+
+int backward_impl(
+    const char* fn, const void* k, const void* v, int64_t k_tok_stride, int64_t v_tok_stride,
     const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens, const float* k_taps,
     const float* v_taps, const float* k_gamma, const float* v_gamma, float eps, const void* k_state,
     const void* v_state, int64_t num_state_slots, const int32_t* state_idx,
@@ -402,8 +406,6 @@ SC_API int shortconv_kv_backward(
     float* dv_gamma, void* dstate_in_k, void* dstate_in_v, void* workspace,
     size_t workspace_bytes, int32_t num_heads, int32_t head_dim, int32_t width, int32_t dtype,
     void* stream) {
-    g_err[0] = 0;
-    const char* fn = "shortconv_kv_backward";
     int rc = check_backward_shape(fn, total_tokens, num_seqs, num_heads, head_dim, width, dtype);
     if (rc != SC_OK) return rc;
     if (!k_taps || !v_taps || !k_gamma || !v_gamma)
@@ -483,6 +485,103 @@ SC_API int shortconv_kv_backward(
     hipError_t e = sc::launch_backward(a, dtype, head_dim, width, (hipStream_t)stream);
     if (e != hipSuccess) return fail(SC_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return SC_OK;
+}
+
+}  // namespace
+
+SC_API int shortconv_kv_backward(
+    const void* k, const void* v, int64_t k_tok_stride, int64_t v_tok_stride,
+    const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens, const float* k_taps,
+    const float* v_taps, const float* k_gamma, const float* v_gamma, float eps, const void* k_state,
+    const void* v_state, int64_t num_state_slots, const int32_t* state_idx,
+    const uint8_t* has_initial_state, const void* dy_k, const void* dy_v, const void* dstate_out_k,
+    const void* dstate_out_v, void* dk, void* dv, float* dk_taps, float* dv_taps, float* dk_gamma,
+    float* dv_gamma, void* dstate_in_k, void* dstate_in_v, void* workspace,
+    size_t workspace_bytes, int32_t num_heads, int32_t head_dim, int32_t width, int32_t dtype,
+    void* stream) {
+    g_err[0] = 0;
+    return backward_impl("shortconv_kv_backward", k, v, k_tok_stride, v_tok_stride, cu_seqlens,
+                         num_seqs, total_tokens, k_taps, v_taps, k_gamma, v_gamma, eps, k_state,
+                         v_state, num_state_slots, state_idx, has_initial_state, dy_k, dy_v,
+                         dstate_out_k, dstate_out_v, dk, dv, dk_taps, dv_taps, dk_gamma, dv_gamma,
+                         dstate_in_k, dstate_in_v, workspace, workspace_bytes, num_heads, head_dim,
+                         width, dtype, stream);
+}
+
+// ------------------------------------------------------------------------------------------------
+// The backward for callers that cannot allocate: its workspace is a file-scope device array, one
+// copy per GPU, held until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory, so its device address is looked up once per device (with that device
+// current) and only that address is handed to the kernels.
+// ------------------------------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[SHORTCONV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// The device address of the current device's scratch array, or null with *code and the message
+// set.
+void* scratch_for_current_device(const char* fn, int* code) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *code = fail(SC_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        *code = fail(SC_ERR_UNSUPPORTED, "%s: device %d beyond the %d this library tracks", fn,
+                     dev, kMaxDevices);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            *code = fail(SC_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s",
+                         fn, dev, hipGetErrorString(e));
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+SC_API int shortconv_kv_backward_noalloc(
+    const void* k, const void* v, int64_t k_tok_stride, int64_t v_tok_stride,
+    const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens, const float* k_taps,
+    const float* v_taps, const float* k_gamma, const float* v_gamma, float eps, const void* k_state,
+    const void* v_state, int64_t num_state_slots, const int32_t* state_idx,
+    const uint8_t* has_initial_state, const void* dy_k, const void* dy_v, const void* dstate_out_k,
+    const void* dstate_out_v, void* dk, void* dv, float* dk_taps, float* dv_taps, float* dk_gamma,
+    float* dv_gamma, void* dstate_in_k, void* dstate_in_v, int32_t num_heads, int32_t head_dim,
+    int32_t width, int32_t dtype, void* stream) {
+    g_err[0] = 0;
+    const char* fn = "shortconv_kv_backward_noalloc";
+    int rc = check_backward_shape(fn, total_tokens, num_seqs, num_heads, head_dim, width, dtype);
+    if (rc != SC_OK) return rc;
+    const size_t need =
+        sc::backward_shape(total_tokens, num_seqs, num_heads, head_dim, width, dtype)
+            .workspace_bytes;
+    if (need > (size_t)SHORTCONV_NOALLOC_SCRATCH_BYTES)
+        return fail(SC_ERR_UNSUPPORTED,
+                    "%s: this problem needs %zu bytes of workspace, more than the %zu bytes of "
+                    "static scratch; use shortconv_kv_backward with a workspace",
+                    fn, need, (size_t)SHORTCONV_NOALLOC_SCRATCH_BYTES);
+    int code = SC_OK;
+    void* ws = scratch_for_current_device(fn, &code);
+    if (!ws) return code;
+    return backward_impl(fn, k, v, k_tok_stride, v_tok_stride, cu_seqlens, num_seqs,
+                         total_tokens, k_taps, v_taps, k_gamma, v_gamma, eps, k_state, v_state,
+                         num_state_slots, state_idx, has_initial_state, dy_k, dy_v, dstate_out_k,
+                         dstate_out_v, dk, dv, dk_taps, dv_taps, dk_gamma, dv_gamma, dstate_in_k,
+                         dstate_in_v, ws, (size_t)SHORTCONV_NOALLOC_SCRATCH_BYTES, num_heads,
+                         head_dim, width, dtype, stream);
 }
 
 SC_API const char* shortconv_last_error(void) { return g_err; }

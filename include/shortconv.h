@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define SHORTCONV_ABI_VERSION 4
+#define SHORTCONV_ABI_VERSION 5
 
 typedef enum {
     SC_DTYPE_F32 = 0,  /* IEEE binary32 */
@@ -269,6 +269,31 @@ int shortconv_kv_backward(const void* k, const void* v, int64_t k_tok_stride, in
 size_t shortconv_kv_backward_workspace_size(int64_t total_tokens, int32_t num_seqs,
                                             int32_t num_heads, int32_t head_dim, int32_t width,
                                             int32_t dtype);
+
+/*
+ * shortconv_kv_backward_noalloc: shortconv_kv_backward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving or training loops, harnesses that forbid
+ * hipMalloc). It takes the same arguments except the workspace, and allocates nothing: its
+ * workspace is a static device array of SHORTCONV_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends (its address is looked up on the first call on each
+ * device). Results are bit-identical to shortconv_kv_backward's.
+ *  - A problem whose workspace (shortconv_kv_backward_workspace_size) exceeds
+ *    SHORTCONV_NOALLOC_SCRATCH_BYTES is rejected with SC_ERR_UNSUPPORTED before anything is
+ *    launched.
+ *  - Every call on one GPU uses that GPU's one array: two calls that may overlap on the same GPU
+ *    (different streams, no ordering) race on it and give undefined results. Order them.
+ */
+#define SHORTCONV_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int shortconv_kv_backward_noalloc(
+    const void* k, const void* v, int64_t k_tok_stride, int64_t v_tok_stride,
+    const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens, const float* k_taps,
+    const float* v_taps, const float* k_gamma, const float* v_gamma, float eps, const void* k_state,
+    const void* v_state, int64_t num_state_slots, const int32_t* state_idx,
+    const uint8_t* has_initial_state, const void* dy_k, const void* dy_v, const void* dstate_out_k,
+    const void* dstate_out_v, void* dk, void* dv, float* dk_taps, float* dv_taps, float* dk_gamma,
+    float* dv_gamma, void* dstate_in_k, void* dstate_in_v, int32_t num_heads, int32_t head_dim,
+    int32_t width, int32_t dtype, void* stream);
 
 /* Message for the last non-zero return on the calling thread ("" if none). Valid until the next
  * call on the same thread. */

@@ -31,6 +31,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["shortconv_abi_version", "shortconv_kv_backward",
+                                    "shortconv_kv_backward_noalloc",
                                     "shortconv_kv_backward_workspace_size", "shortconv_kv_decode",
                                     "shortconv_kv_decode_mxfp8", "shortconv_kv_prefill",
                                     "shortconv_kv_prefill_mxfp8", "shortconv_kv_verify",
@@ -223,3 +224,38 @@ def test_backward_workspace_size(lib):
     assert size(0, 0, 8, 128, 4, 1) == 0
     assert size(10, 2, 8, 96, 4, 1) == 2 ** 64 - 1  # unsupported head_dim -> SIZE_MAX
     assert "head_dim" in lib.shortconv_last_error().decode()
+
+
+def noalloc_args(**over):
+    """shortconv_kv_backward_noalloc's arguments: the backward's without the workspace pair."""
+    a = backward_args(**over)
+    return a[:29] + a[31:]
+
+
+@pytest.mark.parametrize("over,code,msg", [
+    (dict(W=9), UNSUPPORTED, "width"),
+    (dict(n=-1), INVALID, "num_seqs"),
+    # 131072 tokens at width 8 need ~62 MB of partials: beyond the 16 MiB static scratch
+    (dict(T=131072, n=1, W=8), UNSUPPORTED, "static scratch"),
+], ids=["width", "num_seqs", "too_large"])
+def test_noalloc_backward_rejects_before_any_device_call(lib, over, code, msg):
+    from causal_short_convolution_amd import _binding
+    _binding.load_library()
+    rc = lib.shortconv_kv_backward_noalloc(*noalloc_args(**over))
+    assert rc == code
+    err = lib.shortconv_last_error().decode()
+    assert err.startswith("shortconv_kv_backward_noalloc") and msg in err, err
+
+
+def test_mxfp8_entry_points_reject_null_scales(lib):
+    from causal_short_convolution_amd import _binding
+    _binding.load_library()
+    a = prefill_args()
+    # shortconv_kv_prefill_mxfp8: the prefill's arguments with the scale pair after the codes
+    mx = a[:20] + [FAKE, None] + a[20:]
+    assert lib.shortconv_kv_prefill_mxfp8(*mx) == INVALID
+    assert "scale" in lib.shortconv_last_error().decode()
+    d = decode_args()
+    mxd = d[:17] + [None, FAKE] + d[17:]
+    assert lib.shortconv_kv_decode_mxfp8(*mxd) == INVALID
+    assert "scale" in lib.shortconv_last_error().decode()
