@@ -195,6 +195,36 @@ __device__ inline uint32_t e4m3x4_scaled(float v0, float v1, float v2, float v3,
     return __builtin_bit_cast(uint32_t, w);
 }
 
+// The MXFP8 encoding of one lane's VEC values: the maximum over the 32/VEC lanes of a 32-element
+// block (DPP), the E8M0 exponent e = floor(log2(max)) - 8 clamped to [-127, 127] (-127 for an
+// all-zero block), and the saturated E4M3 codes of v * 2^-e.
+template <class E>
+struct MxEnc {
+    uint32_t packed[E::VEC / 4];
+    int e;
+};
+template <class E>
+__device__ inline MxEnc<E> mx_encode(const float (&o)[E::VEC]) {
+    constexpr int VEC = E::VEC;
+    constexpr int LPB = 32 / VEC;
+    float amax = 0.0f;
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) amax = __builtin_fmaxf(amax, __builtin_fabsf(o[v]));
+    amax = __builtin_fmaxf(amax, dpp<kQuadXor1>(amax));
+    amax = __builtin_fmaxf(amax, dpp<kQuadXor2>(amax));
+    if (LPB == 8) amax = __builtin_fmaxf(amax, dpp<kRowHalfMirror>(amax));
+    MxEnc<E> r;
+    int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 1 - 8 : -127;
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    r.e = e;
+    const float scale = __builtin_ldexpf(1.0f, e);
+    const float lim = __builtin_ldexpf(448.0f, e);  // +inf at e = 127: nothing saturates there
+#pragma unroll
+    for (int q = 0; q < VEC / 4; ++q)
+        r.packed[q] = e4m3x4_scaled(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3], scale, lim);
+    return r;
+}
+
 // MXFP8 rows: 32-element blocks along head_dim share one E8M0 scale 2^e with
 // e = floor(log2(max |v|)) - 8 (clamped to [-127, 127]; -127 for an all-zero block), and each
 // element is stored as the E4M3 code of v * 2^-e. Codes [num_slots][H][D] bytes, scales
@@ -218,29 +248,8 @@ struct MxSink {
           scale_off((uint32_t)(((int64_t)h * D + d0) / 32)),
           scale_lane(d0 % 32 == 0),
           num_slots(a.num_slots) {}
-    struct Enc {
-        uint32_t packed[VEC / 4];  // the VEC codes, 4 per word
-        int e;                     // the block's scale exponent
-    };
-    __device__ Enc encode(const float (&o)[VEC]) const {
-        float amax = 0.0f;
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) amax = __builtin_fmaxf(amax, __builtin_fabsf(o[v]));
-        amax = __builtin_fmaxf(amax, dpp<kQuadXor1>(amax));
-        amax = __builtin_fmaxf(amax, dpp<kQuadXor2>(amax));
-        if (LPB == 8) amax = __builtin_fmaxf(amax, dpp<kRowHalfMirror>(amax));
-        Enc r;
-        int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 1 - 8 : -127;
-        e = e < -127 ? -127 : (e > 127 ? 127 : e);
-        r.e = e;
-        const float scale = __builtin_ldexpf(1.0f, e);
-        const float lim = __builtin_ldexpf(448.0f, e);  // +inf at e = 127: nothing saturates there
-#pragma unroll
-        for (int q = 0; q < VEC / 4; ++q)
-            r.packed[q] = e4m3x4_scaled(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3], scale,
-                                        lim);
-        return r;
-    }
+    using Enc = MxEnc<E>;  // the VEC codes, 4 per word, and the block's scale exponent
+    __device__ Enc encode(const float (&o)[VEC]) const { return mx_encode<E>(o); }
     __device__ void write(int64_t slot, bool active, const Enc& enc) const {
         if (!(active && slot >= 0 && slot < num_slots)) return;
         char* row = codes + slot * row_elems + code_off;
@@ -448,6 +457,250 @@ __global__ void __launch_bounds__(kBlock, (span_min_waves<W, MX>())) prefill_ker
                 r = ldrow(dst + e * row_bytes, lane_off);
             if (active && (e != i || !read_state))  // e == i with a read state is a no-op copy
                 strow(dst + i * row_bytes, lane_off, r);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Prefill over column slices that each hold one tensor (H * D a multiple of 64 lanes' worth of
+// elements, so K and V never share a wavefront), for windows of width <= 4.
+//
+// The same tiles, spans, LDS hand-off and row math as prefill_kernel, with these differences:
+//  - every cache store is issued unconditionally through a buffer resource whose range is the
+//    destination row: a slot outside the pool (or a token past the span's end) gets an empty
+//    range and the hardware drops the store. With no load or store under a branch, the compiler
+//    knows exactly how many memory operations follow each row load and waits for that row alone,
+//    so each token's row is stored as soon as it is computed and no finished rows are held in
+//    registers (the MXFP8 variant fits 4 waves per SIMD, against 3 for prefill_kernel);
+//  - the tensor, and so every base address, is wave-uniform;
+//  - the workgroup walks units (tile, slice) g, g + G, ... (slice fastest, G a multiple of the
+//    slice count) with the hand-off buffer alternating between two halves from one unit to the
+//    next, so that a persistent grid can be used; by default G is the number of units (measured
+//    fastest), and each workgroup handles one.
+// ------------------------------------------------------------------------------------------------
+constexpr int kBufferDword3 = 0x00020000;  // raw (untyped, unswizzled) buffer resource, gfx9
+constexpr int kNonTemporal = 2;            // cache policy of the streaming stores
+
+// A resource covering `bytes` bytes at row `row` of `base`, or an empty one (every access out of
+// range, so stores are dropped and loads return zero) when !valid. All arguments wave-uniform.
+__device__ inline __amdgpu_buffer_rsrc_t row_resource(char* base, int64_t row, uint32_t bytes,
+                                                      bool valid) {
+    char* p = base + (valid ? row : 0) * (int64_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, valid ? (int)bytes : 0, kBufferDword3);
+}
+
+// Plain cache rows of one tensor (wave-uniform destination).
+template <class E>
+struct PlainRows {
+    char* cache;
+    uint32_t row_bytes;
+    uint32_t voff;
+    int64_t num_slots;
+    __device__ PlainRows(char* c, uint32_t rb, uint32_t lane_off, int64_t ns)
+        : cache(c), row_bytes(rb), voff(lane_off), num_slots(ns) {}
+    using Enc = uint4;
+    __device__ Enc encode(const float (&o)[E::VEC]) const { return E::narrow(o); }
+    __device__ void write(int64_t slot, const Enc& e) const {
+        const bool ok = slot >= 0 && slot < num_slots;
+        const u32x4 v = {e.x, e.y, e.z, e.w};
+        __builtin_amdgcn_raw_buffer_store_b128(v, row_resource(cache, slot, row_bytes, ok), voff,
+                                               0, kNonTemporal);
+    }
+};
+
+// MXFP8 cache rows of one tensor: the codes row and the scales row each through its own resource;
+// lanes that do not hold a block's first element aim their scale store past the range.
+template <class E>
+struct MxRows {
+    static constexpr int VEC = E::VEC;
+    char* codes;
+    char* scales;
+    uint32_t code_bytes;   // H * D
+    uint32_t scale_bytes;  // H * D / 32
+    uint32_t code_voff;
+    uint32_t scale_voff;
+    int64_t num_slots;
+    __device__ MxRows(char* c, char* sc, uint32_t row_elems, int h, int d0, int D, int64_t ns)
+        : codes(c), scales(sc), code_bytes(row_elems), scale_bytes(row_elems / 32),
+          code_voff((uint32_t)(h * D + d0)),
+          scale_voff(d0 % 32 == 0 ? (uint32_t)((h * D + d0) / 32) : row_elems / 32),
+          num_slots(ns) {}
+    using Enc = MxEnc<E>;
+    __device__ Enc encode(const float (&o)[VEC]) const { return mx_encode<E>(o); }
+    __device__ void write(int64_t slot, const Enc& enc) const {
+        const bool ok = slot >= 0 && slot < num_slots;
+        if (VEC == 8) {
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            const u32x2_t v = {enc.packed[0], enc.packed[VEC / 4 - 1]};
+            __builtin_amdgcn_raw_buffer_store_b64(v, row_resource(codes, slot, code_bytes, ok),
+                                                  code_voff, 0, kNonTemporal);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b32(enc.packed[0],
+                                                  row_resource(codes, slot, code_bytes, ok),
+                                                  code_voff, 0, kNonTemporal);
+        }
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(enc.e + 127),
+                                             row_resource(scales, slot, scale_bytes, ok),
+                                             scale_voff, 0, 0);
+    }
+};
+
+template <class E, bool MX>
+struct RowsFor { using type = PlainRows<E>; };
+template <class E>
+struct RowsFor<E, true> { using type = MxRows<E>; };
+
+#ifndef SC_SLICE_WAVES
+#define SC_SLICE_WAVES 4
+#endif
+#ifndef SC_SLICE_WAVES_MX
+#define SC_SLICE_WAVES_MX 4
+#endif
+
+template <class E, int D, int W, int BT, bool MX>
+__global__ void __launch_bounds__(kBlock, (MX ? SC_SLICE_WAVES_MX : SC_SLICE_WAVES))
+    prefill_slice_kernel(StepArgs a) {
+    constexpr int VEC = E::VEC;
+    constexpr int LPH = D / VEC;
+    constexpr int R = W - 1;
+    constexpr int NW = kBlock / 64;
+    constexpr int BB = NW * BT;
+    static_assert(W <= 4, "narrow windows only");
+    static_assert(BT >= R && BT <= 64, "span length");
+    using Rows = typename RowsFor<E, MX>::type;
+    __shared__ uint4 handoff[2][NW - 1][R > 0 ? R : 1][64];
+
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wl = threadIdx.x & 63;
+    const int slices = a.lane_blocks;
+    const int64_t units = (int64_t)a.tiles * slices;
+    if ((int64_t)blockIdx.x >= units) return;
+    const int slice = uniform((int32_t)(blockIdx.x % slices));
+    // whole slices hold one tensor: the tensor, and everything picked by it, is wave-uniform
+    const int tensor = uniform(slice * 64 >= a.lanes_per_tensor ? 1 : 0);
+    const int c = slice * 64 + wl - tensor * a.lanes_per_tensor;
+    const int h = c / LPH;
+    const int d0 = (c - h * LPH) * VEC;
+    const int64_t T = a.tokens;
+    const char* x = static_cast<const char*>(tensor ? a.x[1] : a.x[0]);
+    const int64_t stride_bytes = (tensor ? a.x_stride[1] : a.x_stride[0]) * E::BYTES;
+    char* state = static_cast<char*>(tensor ? a.state[1] : a.state[0]);
+    const float* taps = tensor ? a.taps[1] : a.taps[0];
+    const int64_t row_bytes = (int64_t)a.heads * D * E::BYTES;
+    const uint32_t lane_off = (uint32_t)(((int64_t)h * D + d0) * E::BYTES);
+    char* stand_in = reinterpret_cast<char*>(const_cast<float*>(taps));  // >= one row long
+    const Rows rows = [&] {
+        if constexpr (MX)
+            return Rows(static_cast<char*>(tensor ? a.cache[1] : a.cache[0]),
+                        static_cast<char*>(tensor ? a.scales[1] : a.scales[0]),
+                        (uint32_t)(a.heads * D), h, d0, D, a.num_slots);
+        else
+            return Rows(static_cast<char*>(tensor ? a.cache[1] : a.cache[0]), (uint32_t)row_bytes,
+                        lane_off, a.num_slots);
+    }();
+
+    LaneParams<E, W> p;
+    load_params<E, W>(taps, tensor ? a.gamma[1] : a.gamma[0], a.heads, D, h, d0, p);
+    const float inv_d = 1.0f / (float)D;
+    int par = 0;
+
+    for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+        const int64_t tile = u / slices;
+        const int s = find_tile_seq<BB>(a.cu, a.num_seqs, T, tile);
+        const int64_t start = uniform((int64_t)clamp_tok(a.cu[s], T));
+        int64_t end = uniform((int64_t)clamp_tok(a.cu[s + 1], T));
+        if (end < start) end = start;
+        const int64_t L = end - start;
+        const int64_t j = tile - tile_base<BB>(a.cu, s, T);
+        const int64_t ntiles = L > 0 ? (L + BB - 1) / BB : 1;
+        if (j < 0 || j >= ntiles) continue;  // the same for the whole workgroup
+
+        const int64_t t0 = start + j * BB + (int64_t)w * BT;
+        const int64_t rem = end - t0;
+        const int n = rem <= 0 ? 0 : (rem < BT ? (int)rem : BT);
+        int32_t idx = -1;
+        bool slot_ok = false, read_state = false;
+        if (j == 0) {
+            idx = uniform(a.state_idx ? a.state_idx[s] : s);
+            slot_ok = R > 0 && state != nullptr && idx >= 0 && idx < a.num_state_slots;
+            read_state = slot_ok && (a.has_init ? a.has_init[s] != 0 : true);
+        }
+        const bool first_span = j == 0 && w == 0;
+
+        // Loads, all issued unconditionally and oldest first in the order of use: the span's
+        // slots (lane i: token i's slot; a span with no rows reads a stand-in word), the halo
+        // (wave 0: the previous tile's last rows or the stored state; the other waves and a fresh
+        // sequence read R stand-in rows and discard them), the rows the next wave needs, then
+        // the other rows (past a short span's end the last row again; a span with no rows reads
+        // the stand-in). The stand-in is the taps array, at least W rows long.
+        const int last = n > 0 ? n - 1 : 0;
+        const int64_t* sp = n > 0 ? a.slot + t0 + (wl < last ? wl : last)
+                                  : reinterpret_cast<const int64_t*>(taps);
+        const int64_t slot_word = *sp;
+        const int64_t lane_slot = wl < n ? slot_word : (int64_t)-1;  // -1: the store is dropped
+        const bool halo_rows = w == 0 && j > 0;
+        const char* hsrc = halo_rows ? x + (t0 - R) * stride_bytes
+                           : (w == 0 && read_state) ? state + (int64_t)idx * R * row_bytes
+                                                    : stand_in;
+        const int64_t hstride = halo_rows ? stride_bytes : row_bytes;
+        uint4 halo[R > 0 ? R : 1];
+#pragma unroll
+        for (int k = 0; k < R; ++k) halo[k] = ldrow_keep(hsrc + k * hstride, lane_off);
+        const char* xb = n > 0 ? x + t0 * stride_bytes : stand_in;
+        const int64_t rstride = n > 0 ? stride_bytes : 0;
+        uint4 raw[BT];
+#pragma unroll
+        for (int i = BT - R; i < BT; ++i)
+            raw[i] = ldrow_keep(xb + (i < last ? i : last) * rstride, lane_off);
+#pragma unroll
+        for (int i = 0; i < BT - R; ++i)
+            raw[i] = ldrow(xb + (i < last ? i : last) * rstride, lane_off);
+
+        if (R > 0) {
+            if (w + 1 < NW) {
+#pragma unroll
+                for (int k = 0; k < R; ++k) handoff[par][w][k][wl] = raw[BT - R + k];
+            }
+            __syncthreads();
+            if (w > 0) {
+#pragma unroll
+                for (int k = 0; k < R; ++k) halo[k] = handoff[par][w - 1][k][wl];
+            }
+            par ^= 1;
+        }
+        if (first_span && !read_state) {
+#pragma unroll
+            for (int k = 0; k < R; ++k) halo[k] = make_uint4(0, 0, 0, 0);
+        }
+        float win[W][VEC];
+#pragma unroll
+        for (int k = 0; k < R; ++k) E::widen(halo[k], win[k]);
+        // Token i's row goes to win[(i + R) % W] (a ring). Every token is computed and its row
+        // stored, tokens past the span's end (recomputing the last row) with an invalid slot,
+        // so the store is dropped: no branch, and each token waits only for its own row.
+#pragma unroll
+        for (int i = 0; i < BT; ++i) {
+            E::widen(raw[i], win[(i + R) % W]);
+            float o[VEC];
+            fused_row<E, W, LPH>(win, i % W, p, a.eps, inv_d, o);
+            rows.write(lane_value(lane_slot, i), rows.encode(o));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // The sequence's first tile writes its new state (its first wave read the old one), as in
+        // prefill_kernel.
+        if (R > 0 && first_span && slot_ok) {
+            char* dst = state + (int64_t)idx * R * row_bytes;
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const int64_t e = L + i;
+                uint4 r = make_uint4(0, 0, 0, 0);
+                if (e >= R)
+                    r = ldrow(x + (start + e - R) * stride_bytes, lane_off);
+                else if (read_state)
+                    r = ldrow(dst + e * row_bytes, lane_off);
+                if (e != i || !read_state) strow(dst + i * row_bytes, lane_off, r);
+            }
         }
     }
 }
@@ -664,6 +917,23 @@ template <class E, int D, int W>
 constexpr KernelFn prefill_fn() { return prefill_kernel<E, D, W, span_tokens<W, false>(), false>; }
 template <class E, int D, int W>
 constexpr KernelFn prefill_mx_fn() { return prefill_kernel<E, D, W, span_tokens<W, true>(), true>; }
+#ifndef SC_SLICE_BT
+#define SC_SLICE_BT 8
+#endif
+#ifndef SC_SLICE_BT_MX
+#define SC_SLICE_BT_MX 8
+#endif
+// the persistent form exists for W <= 4; wider windows map to the one-shot kernel (never used)
+template <class E, int D, int W>
+constexpr KernelFn prefill_slice_fn() {
+    if constexpr (W <= 4) return prefill_slice_kernel<E, D, W, SC_SLICE_BT, false>;
+    else return prefill_kernel<E, D, W, span_tokens<W, false>(), false>;
+}
+template <class E, int D, int W>
+constexpr KernelFn prefill_slice_mx_fn() {
+    if constexpr (W <= 4) return prefill_slice_kernel<E, D, W, SC_SLICE_BT_MX, true>;
+    else return prefill_kernel<E, D, W, span_tokens<W, true>(), true>;
+}
 template <class E, int D, int W>
 constexpr KernelFn decode_fn() { return decode_kernel<E, D, W, false>; }
 template <class E, int D, int W>
@@ -686,6 +956,8 @@ constexpr VerifyFn commit_fn() { return commit_kernel<E, D, W>; }
 const KernelFn kPrefill[2][3][8] = SC_TABLE(prefill);
 const KernelFn kDecode[2][3][8] = SC_TABLE(decode);
 const KernelFn kPrefillMx[2][3][8] = SC_TABLE(prefill_mx);
+const KernelFn kPrefillSlice[2][3][8] = SC_TABLE(prefill_slice);
+const KernelFn kPrefillSliceMx[2][3][8] = SC_TABLE(prefill_slice_mx);
 const KernelFn kDecodeMx[2][3][8] = SC_TABLE(decode_mx);
 const KernelFn kQuantizeMx[2][3] = {
     {mx_quantize_kernel<F32, 64>, mx_quantize_kernel<F32, 128>, mx_quantize_kernel<F32, 256>},
@@ -696,9 +968,36 @@ const VerifyFn kCommit[2][3][8] = SC_TABLE(commit);
 
 int d_index(int D) { return D == 64 ? 0 : (D == 128 ? 1 : 2); }
 
+// Workgroups per compute unit of a persistent prefill_slice_kernel grid; 0 = one workgroup per
+// unit of work. Measured on MI355X (varlen bf16 prefill): one per unit 27.5 us; persistent grids
+// of 2 / 3 / 4 workgroups per CU 30.1 / 28.6 / 28.8 us.
+#ifndef SC_SLICE_WG_PER_CU
+#define SC_SLICE_WG_PER_CU 0
+#endif
+
+// prefill_slice_kernel serves narrow windows over slices that each hold one tensor.
+bool use_slice_kernel(int width, int64_t lanes_per_tensor) {
+    return width <= 4 && lanes_per_tensor % 64 == 0;
+}
+
+int compute_units() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n < 1)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 }  // namespace
 
-int prefill_tile_tokens(int, int, int width, bool mx) {
+int prefill_tile_tokens(int width, bool mx, int64_t lanes_per_tensor) {
+    if (use_slice_kernel(width, lanes_per_tensor)) return (kBlock / 64) * (mx ? SC_SLICE_BT_MX : SC_SLICE_BT);
     const int bt = width <= 4 ? (mx ? span_tokens<1, true>() : span_tokens<1, false>())
                               : (mx ? span_tokens<8, true>() : span_tokens<8, false>());
     return (kBlock / 64) * bt;
@@ -706,12 +1005,25 @@ int prefill_tile_tokens(int, int, int width, bool mx) {
 
 hipError_t launch_prefill(StepArgs a, int dtype, int head_dim, int width, bool mx,
                           hipStream_t stream) {
-    // One workgroup per (tile of 4 spans of tokens, 64-lane (1 KiB) column slice of the
-    // K|V rows); a.lane_blocks carries the number of slices.
+    // Units of work: (tile of 4 spans of tokens, 64-lane column slice of the K|V rows);
+    // a.lane_blocks carries the number of slices. One-shot: one workgroup per unit; persistent:
+    // a grid sized to the chip (a multiple of the slice count) walks the units.
     a.lane_blocks = (int32_t)((2 * (int64_t)a.lanes_per_tensor + 63) / 64);
-    const int64_t blocks = (int64_t)a.tiles * a.lane_blocks;
+    const int64_t units = (int64_t)a.tiles * a.lane_blocks;
+    if (use_slice_kernel(width, a.lanes_per_tensor)) {
+        int64_t grid = units;
+        if (SC_SLICE_WG_PER_CU > 0) {
+            int64_t cap = (int64_t)compute_units() * SC_SLICE_WG_PER_CU;
+            cap = cap / a.lane_blocks * a.lane_blocks;
+            if (cap < a.lane_blocks) cap = a.lane_blocks;
+            grid = units < cap ? units : cap;
+        }
+        const KernelFn k = (mx ? kPrefillSliceMx : kPrefillSlice)[dtype][d_index(head_dim)][width - 1];
+        hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+        return hipGetLastError();
+    }
     const KernelFn k = (mx ? kPrefillMx : kPrefill)[dtype][d_index(head_dim)][width - 1];
-    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL(k, dim3((unsigned)units), dim3(kBlock), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -95,7 +95,7 @@ hipError_t launch_verify(StepArgs a, VerifyArgs va, int dtype, int head_dim, int
 hipError_t launch_commit(StepArgs a, VerifyArgs va, int dtype, int head_dim, int width,
                          hipStream_t stream);
 
-// Tokens per prefill workgroup tile for a (dtype, head_dim, width, cache format) combination.
-int prefill_tile_tokens(int dtype, int head_dim, int width, bool mx);
+// Tokens per prefill tile (4 spans) for a width, cache format and row width in lanes.
+int prefill_tile_tokens(int width, bool mx, int64_t lanes_per_tensor);
 
 }  // namespace sc
