@@ -61,9 +61,13 @@ constexpr int64_t kFillBlocks = 2048;
 #ifndef SC_BWD_BT_F32_WIDE
 #define SC_BWD_BT_F32_WIDE 8    // fp32, W > 1
 #endif
-template <class E, int W>
+#ifndef SC_BWD_BT_BF16_PURE
+#define SC_BWD_BT_BF16_PURE 12  // bf16, W <= 4, single-tensor slices (3 waves per SIMD)
+#endif
+template <class E, int W, bool PURE = false>
 constexpr int bwd_span() {
-    return E::BYTES == 2 ? (W <= 5 ? SC_BWD_BT_BF16 : SC_BWD_BT_BF16_WIDE)
+    return E::BYTES == 2 ? (PURE && W <= 4 ? SC_BWD_BT_BF16_PURE
+                                           : (W <= 5 ? SC_BWD_BT_BF16 : SC_BWD_BT_BF16_WIDE))
                          : (W <= 1 ? SC_BWD_BT_F32 : SC_BWD_BT_F32_WIDE);
 }
 
@@ -124,6 +128,26 @@ struct Quad<BF16> {
     }
     __device__ static Raw zero() { return make_uint2(0, 0); }
 };
+
+// Input-gradient rows stored through a buffer resource whose range is the destination row: a row
+// that must not be written gets an empty range and the hardware drops the store, so the store
+// instruction is issued unconditionally (single-tensor slices, where the destination is uniform).
+constexpr int kBufferDword3 = 0x00020000;  // raw (untyped, unswizzled) buffer resource, gfx9
+constexpr int kNonTemporal = 2;            // cache policy of the streaming stores
+template <class E>
+__device__ inline void store_row(char* base, int64_t row, uint32_t bytes, bool valid,
+                                 uint32_t lane_off, const typename Quad<E>::Raw& v) {
+    char* p = base + (valid ? row : 0) * (int64_t)bytes;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(p, (short)0, valid ? (int)bytes : 0, kBufferDword3);
+    if constexpr (E::BYTES == 2) {
+        const u32x2 w = {v.x, v.y};
+        __builtin_amdgcn_raw_buffer_store_b64(w, r, lane_off, 0, kNonTemporal);
+    } else {
+        const u32x4 w = {v.x, v.y, v.z, v.w};
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, lane_off, 0, kNonTemporal);
+    }
+}
 
 // dc of one token from its window (ring: row k of the window is win[(off + k) % W]) and its
 // output gradient; also returns chat for the gamma gradient. Same arithmetic order as the forward
@@ -186,8 +210,20 @@ __device__ inline void add_state_loss(const typename Quad<E>::Raw (&gsr)[R > 0 ?
     }
 }
 
-template <class E, int D, int W, int BT>
-__global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
+// PURE: every 64-lane slice holds one tensor (H * D a multiple of 256), so the tensor and every
+// destination are wave-uniform and the input-gradient rows are stored as they are computed;
+// otherwise they are held until the span's loop ends (a conditional store between tokens would
+// make the compiler wait for everything in flight).
+#ifndef SC_BWD_WAVES_PURE
+#define SC_BWD_WAVES_PURE 3
+#endif
+template <class E, int W, bool PURE>
+constexpr int bwd_min_waves() {
+    return PURE && W <= 4 && E::BYTES == 2 ? SC_BWD_WAVES_PURE : 2;
+}
+
+template <class E, int D, int W, int BT, bool PURE>
+__global__ void __launch_bounds__(kBwdBlock, (bwd_min_waves<E, W, PURE>())) backward_kernel(BwdArgs a) {
     using Q = Quad<E>;
     using Raw = typename Q::Raw;
     constexpr int LPH = D / 4;
@@ -212,7 +248,8 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
     const int lane = slice * 64 + wl;
     const bool active = lane < 2 * a.lanes_per_tensor;
     const int ln = active ? lane : 0;
-    const int tensor = ln >= a.lanes_per_tensor;
+    const int tensor = PURE ? uniform(slice * 64 >= a.lanes_per_tensor ? 1 : 0)
+                            : (ln >= a.lanes_per_tensor ? 1 : 0);
     const int cch = ln - tensor * a.lanes_per_tensor;
     const int h = cch / LPH;
     const int d0 = (cch - h * LPH) * 4;
@@ -334,7 +371,7 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
             // The tokens issue no store (their results stay in registers until the loop ends), so
             // the compiler waits for each token's rows alone and the first tokens are computed
             // while later rows arrive; a store among them would make it wait for everything.
-            Raw dx_out[BT - R > 0 ? BT - R : 1];
+            Raw dx_out[!PURE && BT - R > 0 ? BT - R : 1];
 #pragma unroll
             for (int i = 0; i < BT; ++i) {
                 float dci[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -356,7 +393,16 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
                 if (i < R)
                     lds[(w * RR + i) * 64 + wl] = make_float4(dci[0], dci[1], dci[2], dci[3]);
                 // rows whose dc window lies inside the span: q = i - R
-                if (i >= R && i - R < n) {
+                if constexpr (PURE) {
+                    if (i >= R) {
+                        const int q = i - R;
+                        float de[4];
+                        row_grad<W>(tap, dcr, q, de);
+                        if (has_tail) add_state_loss<E, R>(gsr, p0 + q - (L - R), de);
+                        store_row<E>(dx, t0 + q, (uint32_t)row_bytes, q < n, lane_off,
+                                     Q::narrow(de));
+                    }
+                } else if (i >= R && i - R < n) {
                     const int q = i - R;
                     float de[4];
                     row_grad<W>(tap, dcr, q, de);
@@ -364,10 +410,12 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
                     dx_out[q] = Q::narrow(de);
                 }
             }
-            if (active) {
+            if constexpr (!PURE) {
+                if (active) {
 #pragma unroll
-                for (int q = 0; q < BT - R; ++q)
-                    if (q < n) Q::store(dx + (t0 + q) * row_bytes + lane_off, dx_out[q]);
+                    for (int q = 0; q < BT - R; ++q)
+                        if (q < n) Q::store(dx + (t0 + q) * row_bytes + lane_off, dx_out[q]);
+                }
             }
             // The initial window's gradient (first span): de[m] = sum_{k<=m} taps[k] dc[m-k],
             // from the span's first R dc, which this wave also left in LDS for its neighbour.
@@ -451,7 +499,11 @@ __global__ void __launch_bounds__(kBwdBlock, 2) backward_kernel(BwdArgs a) {
                         }
                     }
                     if (has_tail) add_state_loss<E, R>(gsr, p0 + q - (L - R), de);
-                    if (active) Q::store(dx + (t0 + q) * row_bytes + lane_off, Q::narrow(de));
+                    if constexpr (PURE)
+                        store_row<E>(dx, t0 + q, (uint32_t)row_bytes, true, lane_off,
+                                     Q::narrow(de));
+                    else if (active)
+                        Q::store(dx + (t0 + q) * row_bytes + lane_off, Q::narrow(de));
                 }
             }
         } else if (first_span && R > 0 && dstate != nullptr) {
@@ -561,14 +613,22 @@ __global__ void __launch_bounds__(256) backward_final_kernel(BwdArgs a, int D, i
 
 using BwdFn = void (*)(BwdArgs);
 template <class E, int D, int W>
-constexpr BwdFn bwd_fn() { return backward_kernel<E, D, W, bwd_span<E, W>()>; }
+constexpr BwdFn bwd_fn() { return backward_kernel<E, D, W, bwd_span<E, W>(), false>; }
+template <class E, int D, int W>
+constexpr BwdFn bwd_pure_fn() { return backward_kernel<E, D, W, bwd_span<E, W, true>(), true>; }
 
-#define SC_BROW(E, D)                                                                      \
-    { bwd_fn<E, D, 1>(), bwd_fn<E, D, 2>(), bwd_fn<E, D, 3>(), bwd_fn<E, D, 4>(),          \
-      bwd_fn<E, D, 5>(), bwd_fn<E, D, 6>(), bwd_fn<E, D, 7>(), bwd_fn<E, D, 8>() }
+#define SC_BROW(K, E, D)                                                                  \
+    { K<E, D, 1>(), K<E, D, 2>(), K<E, D, 3>(), K<E, D, 4>(), K<E, D, 5>(), K<E, D, 6>(),  \
+      K<E, D, 7>(), K<E, D, 8>() }
 const BwdFn kBackward[2][3][8] = {
-    {SC_BROW(F32, 64), SC_BROW(F32, 128), SC_BROW(F32, 256)},
-    {SC_BROW(BF16, 64), SC_BROW(BF16, 128), SC_BROW(BF16, 256)},
+    {SC_BROW(bwd_fn, F32, 64), SC_BROW(bwd_fn, F32, 128), SC_BROW(bwd_fn, F32, 256)},
+    {SC_BROW(bwd_fn, BF16, 64), SC_BROW(bwd_fn, BF16, 128), SC_BROW(bwd_fn, BF16, 256)},
+};
+const BwdFn kBackwardPure[2][3][8] = {
+    {SC_BROW(bwd_pure_fn, F32, 64), SC_BROW(bwd_pure_fn, F32, 128),
+     SC_BROW(bwd_pure_fn, F32, 256)},
+    {SC_BROW(bwd_pure_fn, BF16, 64), SC_BROW(bwd_pure_fn, BF16, 128),
+     SC_BROW(bwd_pure_fn, BF16, 256)},
 };
 using ChunkFn = void (*)(BwdArgs);
 using FinalFn = void (*)(BwdArgs, int, int);
@@ -585,7 +645,10 @@ BwdShape backward_shape(int64_t total_tokens, int32_t num_seqs, int32_t num_head
     BwdShape sh;
     sh.lanes_per_tensor = (int64_t)num_heads * head_dim / 4;
     sh.slices = (2 * sh.lanes_per_tensor + 63) / 64;
-    const int bt = dtype == 1 ? (width <= 5 ? bwd_span<BF16, 1>() : bwd_span<BF16, 8>())
+    const bool pure = sh.lanes_per_tensor % 64 == 0;  // the kernel launch_backward picks
+    const int bt = dtype == 1 ? (pure && width <= 4 ? bwd_span<BF16, 1, true>()
+                                 : width <= 5       ? bwd_span<BF16, 1>()
+                                                    : bwd_span<BF16, 8>())
                               : (width <= 1 ? bwd_span<F32, 1>() : bwd_span<F32, 8>());
     const int64_t bb = (int64_t)kBwdWaves * bt;
     sh.tiles = total_tokens / bb + num_seqs;
@@ -603,8 +666,9 @@ BwdShape backward_shape(int64_t total_tokens, int32_t num_seqs, int32_t num_head
 hipError_t launch_backward(BwdArgs a, int dtype, int head_dim, int width, hipStream_t stream) {
     const int64_t blocks = (int64_t)a.groups * a.slices;
     if (blocks > 0) {
-        hipLaunchKernelGGL(kBackward[dtype][d_index(head_dim)][width - 1], dim3((unsigned)blocks),
-                           dim3(kBwdBlock), 0, stream, a);
+        const bool pure = a.lanes_per_tensor % 64 == 0;
+        hipLaunchKernelGGL((pure ? kBackwardPure : kBackward)[dtype][d_index(head_dim)][width - 1],
+                           dim3((unsigned)blocks), dim3(kBwdBlock), 0, stream, a);
         hipLaunchKernelGGL(kChunkSum[width - 1],
                            dim3((unsigned)(a.slices * (width + 1)), (unsigned)a.chunks), dim3(256),
                            0, stream, a);
