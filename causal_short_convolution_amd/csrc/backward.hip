@@ -44,7 +44,10 @@ constexpr int kBwdWaves = kBwdBlock / 64;
 // Tiles a workgroup walks: at most kMaxTilesPerGroup (bounds each fp32 partial's length), and
 // fewer when that leaves too few workgroups to fill the chip (kFillBlocks).
 constexpr int kMaxTilesPerGroup = 4;
-constexpr int64_t kFillBlocks = 2048;
+#ifndef SC_BWD_FILL_BLOCKS
+#define SC_BWD_FILL_BLOCKS 2048
+#endif
+constexpr int64_t kFillBlocks = SC_BWD_FILL_BLOCKS;
 
 // Span tokens per wave: a span's input and gradient rows are all in flight at once, so wide
 // windows and fp32 rows take shorter spans to stay within the register file. Tuning knobs

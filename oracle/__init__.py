@@ -469,7 +469,9 @@ def compare(got: np.ndarray, y: np.ndarray, cond: np.ndarray, dtype: str):
     """Element-wise acceptance test. ``got`` is stored values (float32 / uint16 bf16 bits).
 
     Returns a dict: ok, worst (max error / bound), max_rel_well_conditioned (plain max relative
-    error over elements with cond <= 8|y|), n."""
+    error over elements with cond <= 8|y|), n, and how far the plain relative criterion alone
+    would be from passing: n_over_rel (elements whose error exceeds tol * |y|, which pass only
+    through the rounding-error floor) and max_rel_over_rel (their largest err / |y|)."""
     g = widen(got)
     err = np.abs(g - y)
     bound = TOL[dtype] * np.abs(y) + FLOOR_ULPS * 2.0 ** -24 * cond
@@ -477,10 +479,14 @@ def compare(got: np.ndarray, y: np.ndarray, cond: np.ndarray, dtype: str):
         ratio = np.where(bound > 0, err / bound, np.where(err > 0, np.inf, 0.0))
         well = cond <= 8.0 * np.abs(y)
         rel = np.where(well & (y != 0), err / np.abs(y), 0.0)
+        over = err > TOL[dtype] * np.abs(y)
+        rel_over = np.where(over, np.where(y != 0, err / np.abs(y), np.inf), 0.0)
     finite = np.isfinite(g).all()
     return {
         "ok": bool(finite and (ratio <= 1.0).all()),
         "worst": float(ratio.max()) if ratio.size else 0.0,
         "max_rel_well_conditioned": float(rel.max()) if rel.size else 0.0,
         "n": int(y.size),
+        "n_over_rel": int(over.sum()),
+        "max_rel_over_rel": float(rel_over.max()) if rel_over.size else 0.0,
     }

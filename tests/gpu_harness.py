@@ -122,7 +122,8 @@ def judge(dw: DeviceWorkload, results=None):
     AssertionError on any violation."""
     w = dw.w
     results = results or oracle_steps(w)
-    report = {"worst": 0.0, "max_rel_well_conditioned": 0.0, "rows": 0}
+    report = {"worst": 0.0, "max_rel_well_conditioned": 0.0, "rows": 0, "elements": 0,
+              "n_over_rel": 0, "max_rel_over_rel": 0.0}
     written = []
     for r in results:
         ok = r.slots >= 0
@@ -142,6 +143,10 @@ def judge(dw: DeviceWorkload, results=None):
                 report["worst"] = max(report["worst"], c["worst"])
                 report["max_rel_well_conditioned"] = max(report["max_rel_well_conditioned"],
                                                          c["max_rel_well_conditioned"])
+                report["elements"] += c["n"]
+                report["n_over_rel"] += c["n_over_rel"]
+                report["max_rel_over_rel"] = max(report["max_rel_over_rel"],
+                                                 c["max_rel_over_rel"])
         report["rows"] += int(slots.size)
     # every other row keeps the sentinel bits
     all_written = np.concatenate(written) if written else np.zeros(0, np.int64)

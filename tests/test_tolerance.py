@@ -101,3 +101,19 @@ def test_nonfinite_fails():
         return g
 
     assert not _check(w, w.steps[0], nan)["ok"]
+
+
+def test_compare_reports_elements_that_pass_only_through_the_floor():
+    # fp32: an exact element, one off by 5e-6 relative (inside tol * |y|), and a cancelled one
+    # (|y| = 1e-6 with a conditioning scale of 4: its error of 1e-7 is far above tol * |y| but
+    # inside the floor 32 * 2^-24 * 4 = 7.6e-6); only the last needs the floor
+    y = np.array([1.0, 2.0, 1e-6])
+    cond = np.array([1.0, 2.0, 4.0])
+    got = np.array([1.0, 2.0 * (1 + 5e-6), 1e-6 + 1e-7], dtype=np.float32)
+    r = oracle.compare(got, y, cond, "f32")
+    assert r["ok"] and r["n"] == 3 and r["n_over_rel"] == 1
+    expect = abs(float(np.float32(1e-6 + 1e-7)) - 1e-6) / 1e-6
+    assert abs(r["max_rel_over_rel"] - expect) < 1e-9
+    # without the cancelled element nothing relies on the floor
+    r2 = oracle.compare(got[:2], y[:2], cond[:2], "f32")
+    assert r2["ok"] and r2["n_over_rel"] == 0 and r2["max_rel_over_rel"] == 0.0
