@@ -3,8 +3,10 @@
 Where floating point decides a code, both sides decide from the same value: the standalone
 quantizer is fed exactly representable inputs, and the fused path is checked against the oracle's
 quantizer applied to the fused kernel's own fp32 output (fp32 I/O, where that output is what the
-plain entry point stores). For bf16 I/O, where the fp32 output is not observable, codes must lie
-within one E4M3 step of the oracle's and scales must agree except at power-of-two boundaries.
+plain entry point stores). For bf16 I/O, where the fp32 output is not observable, a byte may differ
+from the oracle's only where the fp64 value lies within the fp32 error bound of the decision that
+sets it (an E4M3 midpoint or zero for a code, a power of two for a block's scale), and then by one
+step.
 """
 import numpy as np
 import pytest
@@ -148,30 +150,65 @@ def test_fused_mx_equals_quantized_fp32_output(H, D, W):
         assert np.array_equal(to_host(a, "f32"), to_host(b, "f32")), "conv state must not change"
 
 
-def test_fused_mx_bf16_within_one_step_of_oracle():
+def _fp32_bound(y, cond):
+    """Error bound of an fp32 evaluation of the step (the fp32 parity rule of the oracle)."""
+    return oracle.TOL["f32"] * np.abs(y) + oracle.FLOOR_ULPS * 2.0 ** -24 * cond
+
+
+def test_fused_mx_bf16_differs_only_at_decisions_within_fp32_error():
+    """bf16 I/O: the MXFP8 kernel quantizes its fp32 rows, which lie within the fp32 error bound B
+    of the oracle's fp64 rows y. So its bytes equal the oracle quantizer's on y, except where y is
+    within B of a decision: a block whose maximum is within B of a power of two (scale one step
+    apart), or an element whose scaled value is within B of an E4M3 midpoint or of zero (codes one
+    step apart, or the two zeros). Codes are judged under the kernel's own scale."""
     spec = workloads.Spec(dtype="bf16", H=8, D=128, W=4, seed=51, prefill_lens=[300, 17, 1000],
                           has_init=[0, 1, 1], decode_ctx=[9, 70, 2], outlier_p=0.01)
     w = workloads.build(spec)
     plain, mx = _fused_pair(w)
     from gpu_harness import oracle_steps
     res = oracle_steps(w)
+    vals = oracle.e4m3_decode(np.arange(0x00, 0x7F))
+    mids = (vals[:-1] + vals[1:]) / 2.0
+    n_scale = n_code = n_el = 0
     for name, codes_d, scales_d in (("K", mx.k_codes, mx.k_scales), ("V", mx.v_codes, mx.v_scales)):
         codes = codes_d.cpu().numpy()
         scales = scales_d.cpu().numpy()
         for r in res:
             ok = r.slots >= 0
+            if not ok.any():
+                continue
             y = (r.y_k if name == "K" else r.y_v)[ok]
-            ec, es = oracle.mxfp8_quantize(y)
+            b = _fp32_bound(y, (r.cond_k if name == "K" else r.cond_v)[ok])
             gc, gs = codes[r.slots[ok]], scales[r.slots[ok]]
-            blocks = np.abs(y).reshape(*y.shape[:-1], -1, 32).max(-1)
-            near_pow2 = np.abs(np.log2(np.maximum(blocks, 1e-300)) -
-                               np.round(np.log2(np.maximum(blocks, 1e-300)))) < 1e-5
-            assert ((gs == es) | near_pow2).all(), f"{name}: scale differs off a 2^k boundary"
-            same = np.repeat(gs == es, 32, axis=-1)
-            gv, ev = oracle.e4m3_decode(gc), oracle.e4m3_decode(ec)
+            ec, es = oracle.mxfp8_quantize(y)
+            # scales: equal, or one apart with a power of two within B of the block maximum
+            amax = np.abs(y).reshape(*gs.shape, 32).max(-1)
+            bmax = b.reshape(*gs.shape, 32).max(-1)
+            k = np.round(np.log2(np.maximum(amax, 1e-300)))
+            near = np.abs(amax - np.exp2(k)) <= bmax
+            ds = np.abs(gs.astype(int) - es.astype(int))
+            assert ((ds == 0) | ((ds == 1) & near)).all(), f"{name}: scale off a 2^k decision"
+            n_scale += int((ds != 0).sum())
+            # codes under the kernel's scale
+            e = np.repeat(gs.astype(np.int64) - 127, 32, axis=-1)
+            scaled = y * np.exp2(-e.astype(np.float64))
+            bs = b * np.exp2(-e.astype(np.float64))
+            exp_c = oracle.e4m3_encode(scaled)
+            diff = gc != exp_c
+            a = np.abs(scaled)
+            j = np.clip(np.searchsorted(mids, a), 1, len(mids) - 1)
+            dist = np.minimum(np.abs(a - mids[j - 1]), np.abs(a - mids[j]))
+            at_mid = dist <= bs
+            at_zero = a <= bs
+            assert (~diff | at_mid | at_zero).all(), \
+                f"{name}: code differs off a decision at {np.argwhere(diff & ~at_mid & ~at_zero)[:3]}"
+            gv, ev = oracle.e4m3_decode(gc), oracle.e4m3_decode(exp_c)
             step = np.maximum(np.abs(ev) * 2.0 ** -3, 2.0 ** -9)
-            assert (np.abs(gv - ev)[same] <= step[same] * (1 + 1e-9)).all(), f"{name}: codes"
-            assert (gc == ec)[same].mean() > 0.99
+            assert (np.abs(gv - ev)[diff] <= step[diff] * (1 + 1e-12)).all(), f"{name}: > 1 step"
+            n_code += int(diff.sum())
+            n_el += int(y.size)
+    print(f"bytes off the oracle's at fp32-error decisions: {n_scale} scales, {n_code} codes "
+          f"of {n_el}")
     for a, b in ((plain.k_state, mx.k_state), (plain.v_state, mx.v_state)):
         assert np.array_equal(to_host(a, "bf16"), to_host(b, "bf16")), "conv state must not change"
 
