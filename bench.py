@@ -142,7 +142,7 @@ def parse():
                     help="measure the headline workload only (no other workloads, MXFP8 rows, "
                          "speculative verify or backward)")
     ap.add_argument("--only", default=None,
-                    choices=["main", "decode", "mxfp8", "verify", "backward", "copy"],
+                    choices=["main", "decode", "mxfp8", "verify", "backward", "copy", "pattern"],
                     help="run one measurement only (for profiling); prints no JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -453,6 +453,77 @@ def copy_ceiling(torch, bytes_moved, steps, warmup, forms=None):
             "GBps": best["GBps"], "form": best["form"], "forms": table}
 
 
+# Forms of the probe's scatter (see csrc/copy_probe.hip) tried for the same-pattern ceiling.
+SCATTER_FORMS = [(0, 1, "one-shot, 1 token per lane"), (1, 1, "one-shot, 2 tokens per lane"),
+                 (2, 1, "one-shot, 4 tokens per lane"), (3, 1, "one-shot, 8 tokens per lane"),
+                 (4, 2, "persistent 2 WG/CU, 4 tokens per unit, pipelined"),
+                 (4, 4, "persistent 4 WG/CU, 4 tokens per unit, pipelined"),
+                 (5, 1, "fused prefill's memory side, 8 tokens per wave"),
+                 (6, 1, "fused prefill's memory side, 4 tokens per wave")]
+
+
+def pattern_ceiling(torch, w, steps, warmup, forms=None):
+    """Same-pattern ceiling of a workload made of prefill calls: the probe moves each call's K and
+    V rows to their cache rows (row t to row slot[t]) and does nothing else -- no state rows, no
+    halo, no arithmetic -- with the same inputs, replica rotation and graph replay as the fused
+    step. Bytes moved: every row read plus every row written. The fastest form is the ceiling."""
+    import ctypes
+    import numpy as np
+    from causal_short_convolution_amd import build as hip_build
+    assert all(st.kind == "prefill" for st in w.steps)
+    lib = ctypes.CDLL(hip_build.PROBE_LIB)
+    lib.sc_probe_scatter_rows.restype = ctypes.c_int
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.sc_probe_scatter_rows.argtypes = [P, P, I64, I64, P, P, I64, P, I64, I64, I, I, P]
+    item = 2 if w.dtype == "bf16" else 4
+    row_bytes = w.H * w.D * item
+    forms = [f for f in (forms or SCATTER_FORMS) if f[0] < 5 or row_bytes % 1024 == 0]
+    moved = 0
+    for st in w.steps:
+        ok = (st.slot_mapping >= 0) & (st.slot_mapping < w.num_slots)
+        moved += 2 * row_bytes * (len(st.slot_mapping) + int(np.count_nonzero(ok)))
+    n_rep = replica_count(moved)
+    reps = device_replicas(w, torch, n_rep, None, "io")
+
+    def fn(rep, variant, bpc):
+        calls = []
+        for d in rep["steps"]:
+            k, v = d["k"], d["v"]
+            calls.append((P(k.data_ptr()), P(v.data_ptr()), k.stride(0) * item,
+                          v.stride(0) * item, P(rep["k_cache"].data_ptr()),
+                          P(rep["v_cache"].data_ptr()), row_bytes, P(d["slot"].data_ptr()),
+                          k.shape[0], rep["k_cache"].shape[0]))
+
+        def go():
+            stream = P(torch.cuda.current_stream().cuda_stream)
+            for c in calls:
+                rc = lib.sc_probe_scatter_rows(*c, variant, bpc, stream)
+                if rc != 0:
+                    raise RuntimeError(f"sc_probe_scatter_rows failed: {rc}")
+        return go
+
+    table = []
+    for variant, bpc, label in forms:
+        _, dev_ms = time_steps(torch, [fn(r, variant, bpc) for r in reps], steps, warmup,
+                               graph=True)
+        per_ms = dev_ms / steps
+        table.append({"form": label, "kernel_us_mean": round(1e3 * per_ms, 3),
+                      "GBps": round(moved / (per_ms * 1e-3) / 1e9, 1)})
+    best = max(table, key=lambda r: r["GBps"])
+    del reps
+    return {"bytes_moved": moved, "kernel_us_mean": best["kernel_us_mean"], "GBps": best["GBps"],
+            "form": best["form"], "forms": table}
+
+
+def pattern_entry(p, kernel_us):
+    return {"what": "the fastest of several gather/scatter copies of the step's K/V rows to "
+                    "their cache rows alone (no state rows, halo or arithmetic)",
+            "bytes_moved": p["bytes_moved"], "kernel_us_mean": p["kernel_us_mean"],
+            "GBps": p["GBps"], "frac_of_peak": p["GBps"] / HBM_PEAK_GBPS, "form": p["form"],
+            "fused_time_over_pattern_time": kernel_us / p["kernel_us_mean"],
+            "forms": p["forms"]}
+
+
 def calibration_copy(torch):
     n = COPY_BYTES // 2
     src = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").normal_()
@@ -670,6 +741,9 @@ def config_measure(torch, name, args, graph, cache="io"):
         c = copy_ceiling(torch, m["algorithmic_bytes"], args.steps, args.warmup)
         entry["copy_ceiling_GBps"] = c["GBps"]
         entry["kernel_over_copy"] = m["achieved_GBps"] / c["GBps"]
+        if all(st.kind == "prefill" for st in w.steps):
+            p = pattern_ceiling(torch, w, args.steps, args.warmup)
+            entry["pattern_ceiling"] = pattern_entry(p, m["kernel_us_mean"])
     return w, entry
 
 
@@ -721,6 +795,10 @@ def main():
             m = measure(torch, w, 1, 0, reseed_main, graph)
             m = copy_ceiling(torch, m["algorithmic_bytes"], args.steps, args.warmup)
             m["achieved_GBps"] = m["GBps"]
+        elif args.only == "pattern":
+            m = pattern_ceiling(torch, w, args.steps, args.warmup)
+            m["achieved_GBps"] = m["GBps"]
+            print(json.dumps(m["forms"]), flush=True)
         else:
             m = measure_verify(torch, args.steps, args.warmup, args.seed, graph)
         print(f"bench.py: {args.only}: {m['kernel_us_mean']:.2f} us per step, "
@@ -784,6 +862,11 @@ def main():
         calibration_copy(torch)
     progress(f"{n}: same-bytes copy")
     ceil = copy_ceiling(torch, main_m["algorithmic_bytes"], args.steps, args.warmup)
+    pattern = None
+    if all(st.kind == "prefill" for st in w.steps):
+        progress(f"{n}: same-pattern copy")
+        pattern = pattern_entry(pattern_ceiling(torch, w, args.steps, args.warmup),
+                                main_m["kernel_us_mean"])
 
     traffic = None
     if os.path.exists(TRAFFIC_SUMMARY) and args.workload == "varlen_prefill":
@@ -829,6 +912,7 @@ def main():
                          "frac_of_peak": ceil["GBps"] / HBM_PEAK_GBPS,
                          "kernel_over_copy": main_m["achieved_GBps"] / ceil["GBps"],
                          "forms": ceil["forms"]},
+        **({"pattern_ceiling": pattern} if pattern else {}),
         **extra,
     }
     if not args.no_cpu_baseline:

@@ -556,16 +556,24 @@ struct RowsFor<E, true> { using type = MxRows<E>; };
 #ifndef SC_SLICE_WAVES_MX
 #define SC_SLICE_WAVES_MX 4
 #endif
+// Windows of 5 and 6 fit 3 waves per SIMD in registers, 7 and 8 only 2.
+#ifndef SC_SLICE_WAVES_WIDE
+#define SC_SLICE_WAVES_WIDE 2
+#endif
+
+template <int W, bool MX>
+constexpr int slice_min_waves() {
+    return W <= 4 ? (MX ? SC_SLICE_WAVES_MX : SC_SLICE_WAVES) : (W <= 6 ? 3 : SC_SLICE_WAVES_WIDE);
+}
 
 template <class E, int D, int W, int BT, bool MX>
-__global__ void __launch_bounds__(kBlock, (MX ? SC_SLICE_WAVES_MX : SC_SLICE_WAVES))
+__global__ void __launch_bounds__(kBlock, (slice_min_waves<W, MX>()))
     prefill_slice_kernel(StepArgs a) {
     constexpr int VEC = E::VEC;
     constexpr int LPH = D / VEC;
     constexpr int R = W - 1;
     constexpr int NW = kBlock / 64;
     constexpr int BB = NW * BT;
-    static_assert(W <= 4, "narrow windows only");
     static_assert(BT >= R && BT <= 64, "span length");
     using Rows = typename RowsFor<E, MX>::type;
     __shared__ uint4 handoff[2][NW - 1][R > 0 ? R : 1][64];
@@ -923,15 +931,34 @@ constexpr KernelFn prefill_mx_fn() { return prefill_kernel<E, D, W, span_tokens<
 #ifndef SC_SLICE_BT_MX
 #define SC_SLICE_BT_MX 8
 #endif
-// the persistent form exists for W <= 4; wider windows map to the one-shot kernel (never used)
+#ifndef SC_SLICE_BT_WIDE
+#define SC_SLICE_BT_WIDE 8
+#endif
+#ifndef SC_SLICE_BT_WIDE_MX
+#define SC_SLICE_BT_WIDE_MX 8
+#endif
+// Widest window served by prefill_slice_kernel; wider ones use prefill_kernel. Measured on
+// MI355X (bf16, W = 8, 131072 tokens, 8 x 128 heads, one process): prefill_kernel (16-token
+// spans held until every row is in, 2 waves per SIMD) 172.8 us; prefill_slice_kernel at 2 waves
+// per SIMD with 16-token spans 179.8 us, with 8-token spans 223.8 us (at 3 waves per SIMD its
+// registers spill). MXFP8 rows: 185.4 / 186.4 / 219.8 us.
+#ifndef SC_SLICE_MAX_W
+#define SC_SLICE_MAX_W 4
+#endif
+template <int W, bool MX>
+constexpr int slice_span_tokens() {
+    return W <= 4 ? (MX ? SC_SLICE_BT_MX : SC_SLICE_BT) : (MX ? SC_SLICE_BT_WIDE_MX : SC_SLICE_BT_WIDE);
+}
 template <class E, int D, int W>
 constexpr KernelFn prefill_slice_fn() {
-    if constexpr (W <= 4) return prefill_slice_kernel<E, D, W, SC_SLICE_BT, false>;
+    if constexpr (W <= SC_SLICE_MAX_W)
+        return prefill_slice_kernel<E, D, W, slice_span_tokens<W, false>(), false>;
     else return prefill_kernel<E, D, W, span_tokens<W, false>(), false>;
 }
 template <class E, int D, int W>
 constexpr KernelFn prefill_slice_mx_fn() {
-    if constexpr (W <= 4) return prefill_slice_kernel<E, D, W, SC_SLICE_BT_MX, true>;
+    if constexpr (W <= SC_SLICE_MAX_W)
+        return prefill_slice_kernel<E, D, W, slice_span_tokens<W, true>(), true>;
     else return prefill_kernel<E, D, W, span_tokens<W, true>(), true>;
 }
 template <class E, int D, int W>
@@ -975,9 +1002,9 @@ int d_index(int D) { return D == 64 ? 0 : (D == 128 ? 1 : 2); }
 #define SC_SLICE_WG_PER_CU 0
 #endif
 
-// prefill_slice_kernel serves narrow windows over slices that each hold one tensor.
+// prefill_slice_kernel serves windows up to SC_SLICE_MAX_W over slices that each hold one tensor.
 bool use_slice_kernel(int width, int64_t lanes_per_tensor) {
-    return width <= 4 && lanes_per_tensor % 64 == 0;
+    return width <= SC_SLICE_MAX_W && lanes_per_tensor % 64 == 0;
 }
 
 int compute_units() {
@@ -997,7 +1024,11 @@ int compute_units() {
 }  // namespace
 
 int prefill_tile_tokens(int width, bool mx, int64_t lanes_per_tensor) {
-    if (use_slice_kernel(width, lanes_per_tensor)) return (kBlock / 64) * (mx ? SC_SLICE_BT_MX : SC_SLICE_BT);
+    if (use_slice_kernel(width, lanes_per_tensor)) {
+        const int bt = width <= 4 ? (mx ? slice_span_tokens<1, true>() : slice_span_tokens<1, false>())
+                                  : (mx ? slice_span_tokens<8, true>() : slice_span_tokens<8, false>());
+        return (kBlock / 64) * bt;
+    }
     const int bt = width <= 4 ? (mx ? span_tokens<1, true>() : span_tokens<1, false>())
                               : (mx ? span_tokens<8, true>() : span_tokens<8, false>());
     return (kBlock / 64) * bt;
