@@ -50,8 +50,12 @@ KERNEL_SRC = [os.path.join(ROOT, "causal_short_convolution_amd", "csrc", f)
               for f in ("kernels.hip", "device_common.h")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "varlen_bf16_all_kernels_traffic.md")
 COPY_BYTES = 512 << 20          # calibration copy: 512 MiB read + 512 MiB written
-KERNELS = ("prefill_kernel", "decode_kernel", "verify_kernel", "commit_kernel",
-           "mx_quantize_kernel", "backward_kernel", "backward_chunk_kernel", "backward_final_kernel")
+KERNELS = ("prefill_kernel", "prefill_slice_kernel", "decode_kernel", "verify_kernel",
+           "commit_kernel", "mx_quantize_kernel", "backward_kernel", "backward_chunk_kernel",
+           "backward_final_kernel")
+# DRAM-side request sizes on gfx950, as the calibration copy shows (512 MiB read in 4 Mi
+# TCC_EA0_RDREQ_DRAM requests, 512 MiB written in 8 Mi TCC_EA0_WRREQ_DRAM requests)
+DRAM_RD_BYTES, DRAM_WR_BYTES = 128, 64
 
 
 def kernel_source_sha():
@@ -682,19 +686,30 @@ def summarize_profile(dirs):
                                f"avg_ns={float(row['AverageNs']):10.1f} "
                                f"min_ns={row['MinNs']:>8s} max_ns={row['MaxNs']:>8s}")
         for path in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
-            durs = {}
+            # one line per (kernel, grid): a kernel that serves several workloads (of different
+            # shapes) gets one line for each
+            durs, res = {}, {}
             with open(path) as f:
                 for row in csv.DictReader(f):
                     ns = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
-                    durs.setdefault(short(row["Kernel_Name"]), []).append(ns)
-            out.append(f"per-dispatch durations ({os.path.relpath(path, ROOT)}):")
-            for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+                    name = short(row["Kernel_Name"]).split("(")[0]
+                    grid = "x".join(row[c] for c in ("Grid_Size_X", "Grid_Size_Y") if c in row)
+                    durs.setdefault((name, grid), []).append(ns)
+                    res[name] = (row.get("VGPR_Count"), row.get("LDS_Block_Size"),
+                                 row.get("Scratch_Size"))
+            out.append(f"per-dispatch durations by kernel and grid ({os.path.relpath(path, ROOT)}):")
+            for (name, grid), v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
                 v = sorted(v)
 
                 def q(f, v=v):
                     return v[min(len(v) - 1, int(f * len(v)))]
-                out.append(f"  {name[:60]:60s} n={len(v):>5d} mean_ns={sum(v) / len(v):10.1f} "
-                           f"p10_ns={q(0.1):>8d} median_ns={q(0.5):>8d} p90_ns={q(0.9):>8d}")
+                out.append(f"  {name[:56]:56s} grid={grid:>11s} n={len(v):>5d} "
+                           f"mean_ns={sum(v) / len(v):10.1f} p10_ns={q(0.1):>8d} "
+                           f"median_ns={q(0.5):>8d} p90_ns={q(0.9):>8d}")
+            out.append("kernel resources (VGPRs, LDS bytes, scratch bytes per lane):")
+            for name, (vg, lds, scr) in sorted(res.items()):
+                if any(k in name for k in KERNELS):
+                    out.append(f"  {name[:56]:56s} vgpr={vg} lds={lds} scratch={scr}")
         for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"),
                                      recursive=True)):
             with open(path) as f:
@@ -713,14 +728,36 @@ def summarize_profile(dirs):
             factors[ctr] = known_kib / (sum(copies) / len(copies))
             out.append(f"calibration copy {ctr}: {sum(copies) / len(copies):.1f} KiB per dispatch "
                        f"for {known_kib:.0f} KiB moved -> factor {factors[ctr]:.4f}")
+    dram = {}
+    for ctr, size in (("TCC_EA0_RDREQ_DRAM_sum", DRAM_RD_BYTES),
+                      ("TCC_EA0_WRREQ_DRAM_sum", DRAM_WR_BYTES)):
+        copies = sorted(per.get(("copy", ctr), []))[-5:]
+        if copies:
+            mean = sum(copies) / len(copies)
+            dram[ctr] = size
+            out.append(f"calibration copy {ctr}: {mean:.0f} requests per dispatch x {size} B = "
+                       f"{mean * size / COPY_BYTES:.4f} x the {COPY_BYTES} bytes moved")
+
+    def mean(kind, ctr):
+        v = per.get((kind, ctr))
+        return sum(v) / len(v) if v else None
     for kind in sorted({k for k, _ in per if k != "copy"}):
-        vals = {c: per.get((kind, c)) for c in ("FETCH_SIZE", "WRITE_SIZE")}
-        if all(vals.values()) and len(factors) == 2:
-            f_kib = sum(vals["FETCH_SIZE"]) / len(vals["FETCH_SIZE"])
-            w_kib = sum(vals["WRITE_SIZE"]) / len(vals["WRITE_SIZE"])
+        f_kib, w_kib = mean(kind, "FETCH_SIZE"), mean(kind, "WRITE_SIZE")
+        if f_kib is not None and w_kib is not None and len(factors) == 2:
             tr = 1024.0 * (f_kib * factors["FETCH_SIZE"] + w_kib * factors["WRITE_SIZE"])
             out.append(f"{kind}: FETCH_SIZE {f_kib:.1f} KiB, WRITE_SIZE {w_kib:.1f} KiB per "
                        f"dispatch -> {tr:.0f} HBM bytes per launch (calibrated)")
+        rd, wr = mean(kind, "TCC_EA0_RDREQ_DRAM_sum"), mean(kind, "TCC_EA0_WRREQ_DRAM_sum")
+        if rd is not None and wr is not None:
+            out.append(f"{kind}: DRAM requests {rd:.0f} read x {DRAM_RD_BYTES} B + {wr:.0f} write x "
+                       f"{DRAM_WR_BYTES} B = {rd * DRAM_RD_BYTES + wr * DRAM_WR_BYTES:.0f} bytes per "
+                       f"dispatch ({rd * DRAM_RD_BYTES:.0f} read, {wr * DRAM_WR_BYTES:.0f} written)")
+        waves, valu = mean(kind, "SQ_WAVES"), mean(kind, "SQ_INSTS_VALU")
+        if waves and valu is not None:
+            out.append(f"{kind}: {valu / waves:.1f} VALU instructions per wave")
+        others = sorted({c for k, c in per if k == kind})
+        out.append(f"{kind}: counters (mean per dispatch): " + ", ".join(
+            f"{c} {mean(kind, c):.1f}" for c in others))
     print("\n".join(out))
 
 

@@ -561,18 +561,28 @@ struct RowsFor<E, true> { using type = MxRows<E>; };
 #define SC_SLICE_WAVES_WIDE 2
 #endif
 
+// Waves per workgroup of prefill_slice_kernel: a tile is this many consecutive spans of one
+// column slice (the halo of each span after the first comes through LDS). Measured on MI355X
+// (varlen bf16 prefill, one process): 4 waves x 8-token spans 28.2 us; 8 x 4 33.6 us; 16 x 4
+// 35.2 us; 8 x 8 29.4 us. Shorter spans keep fewer rows in flight per wave, and that costs more
+// than the shorter tail of the grid gains.
+#ifndef SC_SLICE_NW
+#define SC_SLICE_NW 4
+#endif
+constexpr int kSliceBlock = 64 * SC_SLICE_NW;
+
 template <int W, bool MX>
 constexpr int slice_min_waves() {
     return W <= 4 ? (MX ? SC_SLICE_WAVES_MX : SC_SLICE_WAVES) : (W <= 6 ? 3 : SC_SLICE_WAVES_WIDE);
 }
 
 template <class E, int D, int W, int BT, bool MX>
-__global__ void __launch_bounds__(kBlock, (slice_min_waves<W, MX>()))
+__global__ void __launch_bounds__(kSliceBlock, (slice_min_waves<W, MX>()))
     prefill_slice_kernel(StepArgs a) {
     constexpr int VEC = E::VEC;
     constexpr int LPH = D / VEC;
     constexpr int R = W - 1;
-    constexpr int NW = kBlock / 64;
+    constexpr int NW = kSliceBlock / 64;
     constexpr int BB = NW * BT;
     static_assert(BT >= R && BT <= 64, "span length");
     using Rows = typename RowsFor<E, MX>::type;
@@ -1027,7 +1037,7 @@ int prefill_tile_tokens(int width, bool mx, int64_t lanes_per_tensor) {
     if (use_slice_kernel(width, lanes_per_tensor)) {
         const int bt = width <= 4 ? (mx ? slice_span_tokens<1, true>() : slice_span_tokens<1, false>())
                                   : (mx ? slice_span_tokens<8, true>() : slice_span_tokens<8, false>());
-        return (kBlock / 64) * bt;
+        return SC_SLICE_NW * bt;
     }
     const int bt = width <= 4 ? (mx ? span_tokens<1, true>() : span_tokens<1, false>())
                               : (mx ? span_tokens<8, true>() : span_tokens<8, false>());
@@ -1050,7 +1060,7 @@ hipError_t launch_prefill(StepArgs a, int dtype, int head_dim, int width, bool m
             grid = units < cap ? units : cap;
         }
         const KernelFn k = (mx ? kPrefillSliceMx : kPrefillSlice)[dtype][d_index(head_dim)][width - 1];
-        hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kBlock), 0, stream, a);
+        hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kSliceBlock), 0, stream, a);
         return hipGetLastError();
     }
     const KernelFn k = (mx ? kPrefillMx : kPrefill)[dtype][d_index(head_dim)][width - 1];
