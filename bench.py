@@ -48,7 +48,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
 MALL_BYTES = 256 << 20          # MI355X Infinity Cache
 KERNEL_SRC = [os.path.join(ROOT, "causal_short_convolution_amd", "csrc", f)
               for f in ("kernels.hip", "device_common.h")]
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "varlen_bf16_all_kernels_traffic.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_kernels_traffic.md")
 COPY_BYTES = 512 << 20          # calibration copy: 512 MiB read + 512 MiB written
 KERNELS = ("prefill_kernel", "prefill_slice_kernel", "decode_kernel", "verify_kernel",
            "commit_kernel", "mx_quantize_kernel", "backward_kernel", "backward_chunk_kernel",
@@ -706,7 +706,8 @@ def summarize_profile(dirs):
                 out.append(f"  {name[:56]:56s} grid={grid:>11s} n={len(v):>5d} "
                            f"mean_ns={sum(v) / len(v):10.1f} p10_ns={q(0.1):>8d} "
                            f"median_ns={q(0.5):>8d} p90_ns={q(0.9):>8d}")
-            out.append("kernel resources (VGPRs, LDS bytes, scratch bytes per lane):")
+            out.append("kernel resources as the tracer reports them (VGPR_Count in its own units: half "
+                       "the assembler's .vgpr_count on this build; LDS and scratch bytes):")
             for name, (vg, lds, scr) in sorted(res.items()):
                 if any(k in name for k in KERNELS):
                     out.append(f"  {name[:56]:56s} vgpr={vg} lds={lds} scratch={scr}")
@@ -905,7 +906,7 @@ def main():
         pattern = pattern_entry(pattern_ceiling(torch, w, args.steps, args.warmup),
                                 main_m["kernel_us_mean"])
 
-    traffic = None
+    traffic = traffic_dram = None
     if os.path.exists(TRAFFIC_SUMMARY) and args.workload == "varlen_prefill":
         txt = open(TRAFFIC_SUMMARY).read()
         kv = dict(line.split(":", 1) for line in txt.splitlines() if line.startswith("- ")
@@ -913,6 +914,7 @@ def main():
         kv = {k[2:].strip(): v.strip() for k, v in kv.items()}
         if kv.get("kernel_source_sha256") == kernel_source_sha():
             traffic = float(kv["hbm_bytes_per_launch"])
+            traffic_dram = float(kv["dram_side_bytes_per_launch"])
 
     line = {
         "metric": METRIC,
@@ -937,6 +939,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": main_m["achieved_GBps"], "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": main_m["achieved_GBps"] / HBM_PEAK_GBPS,
                      "traffic": traffic,
+                     # the same launch's bytes from the DRAM-side request counters
+                     "traffic_dram_side": traffic_dram,
                      "kernel": "+".join(f"{x.kind}_kernel" for x in w.steps),
                      "algorithmic_bytes_per_launch": main_m["algorithmic_bytes"],
                      "kernel_us_mean": main_m["kernel_us_mean"],
