@@ -570,6 +570,17 @@ struct RowsFor<E, true> { using type = MxRows<E>; };
 #define SC_SLICE_NW 4
 #endif
 constexpr int kSliceBlock = 64 * SC_SLICE_NW;
+// 1: a span's halo comes from the previous wave of its workgroup through LDS; 0: every wave loads
+// its own halo rows, which the previous wave of the same workgroup is fetching at the same time
+// (no workgroup barrier). For plain and for MXFP8 rows. Measured on MI355X, one process, LDS /
+// own rows: bf16 rows, varlen 27.7 / 27.4 us, mixed 347.8 / 360.5 us; MXFP8 rows (6 rounds),
+// varlen 25.6 / 25.2 us, mixed 325.5 / 320.8 us.
+#ifndef SC_SLICE_LDS_HALO
+#define SC_SLICE_LDS_HALO 1
+#endif
+#ifndef SC_SLICE_LDS_HALO_MX
+#define SC_SLICE_LDS_HALO_MX 0
+#endif
 
 template <int W, bool MX>
 constexpr int slice_min_waves() {
@@ -586,7 +597,8 @@ __global__ void __launch_bounds__(kSliceBlock, (slice_min_waves<W, MX>()))
     constexpr int BB = NW * BT;
     static_assert(BT >= R && BT <= 64, "span length");
     using Rows = typename RowsFor<E, MX>::type;
-    __shared__ uint4 handoff[2][NW - 1][R > 0 ? R : 1][64];
+    constexpr bool kLdsHalo = MX ? SC_SLICE_LDS_HALO_MX : SC_SLICE_LDS_HALO;
+    __shared__ uint4 handoff[kLdsHalo ? 2 : 1][kLdsHalo ? NW - 1 : 1][R > 0 && kLdsHalo ? R : 1][64];
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wl = threadIdx.x & 63;
@@ -647,8 +659,9 @@ __global__ void __launch_bounds__(kSliceBlock, (slice_min_waves<W, MX>()))
 
         // Loads, all issued unconditionally and oldest first in the order of use: the span's
         // slots (lane i: token i's slot; a span with no rows reads a stand-in word), the halo
-        // (wave 0: the previous tile's last rows or the stored state; the other waves and a fresh
-        // sequence read R stand-in rows and discard them), the rows the next wave needs, then
+        // (the R rows before the span, for wave 0 only when the others get theirs through LDS;
+        // the stored state for a sequence's first span; otherwise R stand-in rows, discarded),
+        // the rows the next wave needs, then
         // the other rows (past a short span's end the last row again; a span with no rows reads
         // the stand-in). The stand-in is the taps array, at least W rows long.
         const int last = n > 0 ? n - 1 : 0;
@@ -656,7 +669,8 @@ __global__ void __launch_bounds__(kSliceBlock, (slice_min_waves<W, MX>()))
                                   : reinterpret_cast<const int64_t*>(taps);
         const int64_t slot_word = *sp;
         const int64_t lane_slot = wl < n ? slot_word : (int64_t)-1;  // -1: the store is dropped
-        const bool halo_rows = w == 0 && j > 0;
+        // with the LDS hand-off only wave 0 reads its halo rows; otherwise every wave with rows
+        const bool halo_rows = kLdsHalo ? (w == 0 && j > 0) : (!first_span && n > 0);
         const char* hsrc = halo_rows ? x + (t0 - R) * stride_bytes
                            : (w == 0 && read_state) ? state + (int64_t)idx * R * row_bytes
                                                     : stand_in;
@@ -674,7 +688,7 @@ __global__ void __launch_bounds__(kSliceBlock, (slice_min_waves<W, MX>()))
         for (int i = 0; i < BT - R; ++i)
             raw[i] = ldrow(xb + (i < last ? i : last) * rstride, lane_off);
 
-        if (R > 0) {
+        if constexpr (kLdsHalo && R > 0) {
             if (w + 1 < NW) {
 #pragma unroll
                 for (int k = 0; k < R; ++k) handoff[par][w][k][wl] = raw[BT - R + k];
