@@ -116,6 +116,10 @@ template <int CTRL>
 __device__ inline float dpp(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
 }
+template <int CTRL>
+__device__ inline uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, true);
+}
 constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141; // lane i <-> 7-i within each half row

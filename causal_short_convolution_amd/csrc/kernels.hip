@@ -189,7 +189,9 @@ __device__ inline uint32_t e4m3x4_scaled(float v0, float v1, float v2, float v3,
     v1 = __builtin_amdgcn_fmed3f(v1, -lim, lim);
     v2 = __builtin_amdgcn_fmed3f(v2, -lim, lim);
     v3 = __builtin_amdgcn_fmed3f(v3, -lim, lim);
-    sc_i16x2 w = {0, 0};
+    // the two conversions write the low and the high half; the word they start from (any
+    // register at hand) is overwritten entirely
+    sc_i16x2 w = __builtin_bit_cast(sc_i16x2, __float_as_uint(v0));
     w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, v0, v1, scale, false);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, v2, v3, scale, true);
     return __builtin_bit_cast(uint32_t, w);
@@ -197,7 +199,11 @@ __device__ inline uint32_t e4m3x4_scaled(float v0, float v1, float v2, float v3,
 
 // The MXFP8 encoding of one lane's VEC values: the maximum over the 32/VEC lanes of a 32-element
 // block (DPP), the E8M0 exponent e = floor(log2(max)) - 8 clamped to [-127, 127] (-127 for an
-// all-zero block), and the saturated E4M3 codes of v * 2^-e.
+// all-zero block), and the saturated E4M3 codes of v * 2^-e. The maximum of magnitudes is taken
+// on their bit patterns, which order non-negative finite floats as unsigned integers do; the
+// pattern's exponent field E gives floor(log2(max)) = E - 127 for a normal maximum, so
+// e = E - 135, which is at most 119, and every zero or subnormal maximum (E = 0) falls to the
+// clamp at -127.
 template <class E>
 struct MxEnc {
     uint32_t packed[E::VEC / 4];
@@ -210,12 +216,12 @@ __device__ inline MxEnc<E> mx_encode(const float (&o)[E::VEC]) {
     float amax = 0.0f;
 #pragma unroll
     for (int v = 0; v < VEC; ++v) amax = __builtin_fmaxf(amax, __builtin_fabsf(o[v]));
-    amax = __builtin_fmaxf(amax, dpp<kQuadXor1>(amax));
-    amax = __builtin_fmaxf(amax, dpp<kQuadXor2>(amax));
-    if (LPB == 8) amax = __builtin_fmaxf(amax, dpp<kRowHalfMirror>(amax));
+    uint32_t bits = __float_as_uint(amax);
+    bits = max(bits, dpp_u32<kQuadXor1>(bits));
+    bits = max(bits, dpp_u32<kQuadXor2>(bits));
+    if (LPB == 8) bits = max(bits, dpp_u32<kRowHalfMirror>(bits));
     MxEnc<E> r;
-    int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 1 - 8 : -127;
-    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    const int e = max((int)(bits >> 23) - 135, -127);
     r.e = e;
     const float scale = __builtin_ldexpf(1.0f, e);
     const float lim = __builtin_ldexpf(448.0f, e);  // +inf at e = 127: nothing saturates there
