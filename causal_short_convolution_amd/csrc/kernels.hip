@@ -570,8 +570,9 @@ struct RowsFor<E, true> { using type = MxRows<E>; };
 // Waves per workgroup of prefill_slice_kernel: a tile is this many consecutive spans of one
 // column slice (the halo of each span after the first comes through LDS). Measured on MI355X
 // (varlen bf16 prefill, one process): 4 waves x 8-token spans 28.2 us; 8 x 4 33.6 us; 16 x 4
-// 35.2 us; 8 x 8 29.4 us. Shorter spans keep fewer rows in flight per wave, and that costs more
-// than the shorter tail of the grid gains.
+// 35.2 us; 8 x 8 29.4 us; 2 x 8 28.8 us; 1 x 8 (each wave reading its own halo) 30.8 us. Shorter
+// spans keep fewer rows in flight per wave, and that costs more than the shorter tail of the grid
+// gains; smaller workgroups re-read more halo rows from other workgroups.
 #ifndef SC_SLICE_NW
 #define SC_SLICE_NW 4
 #endif
@@ -603,7 +604,7 @@ __global__ void __launch_bounds__(kSliceBlock, (slice_min_waves<W, MX>()))
     constexpr int BB = NW * BT;
     static_assert(BT >= R && BT <= 64, "span length");
     using Rows = typename RowsFor<E, MX>::type;
-    constexpr bool kLdsHalo = MX ? SC_SLICE_LDS_HALO_MX : SC_SLICE_LDS_HALO;
+    constexpr bool kLdsHalo = NW > 1 && (MX ? SC_SLICE_LDS_HALO_MX : SC_SLICE_LDS_HALO);
     __shared__ uint4 handoff[kLdsHalo ? 2 : 1][kLdsHalo ? NW - 1 : 1][R > 0 && kLdsHalo ? R : 1][64];
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
