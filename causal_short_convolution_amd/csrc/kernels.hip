@@ -199,11 +199,11 @@ __device__ inline uint32_t e4m3x4_scaled(float v0, float v1, float v2, float v3,
 
 // The MXFP8 encoding of one lane's VEC values: the maximum over the 32/VEC lanes of a 32-element
 // block (DPP), the E8M0 exponent e = floor(log2(max)) - 8 clamped to [-127, 127] (-127 for an
-// all-zero block), and the saturated E4M3 codes of v * 2^-e. The maximum of magnitudes is taken
-// on their bit patterns, which order non-negative finite floats as unsigned integers do; the
-// pattern's exponent field E gives floor(log2(max)) = E - 127 for a normal maximum, so
-// e = E - 135, which is at most 119, and every zero or subnormal maximum (E = 0) falls to the
-// clamp at -127.
+// all-zero block), and the saturated E4M3 codes of v * 2^-e. Across lanes the maximum of the
+// magnitudes is taken on their bit patterns, which order non-negative finite floats as unsigned
+// integers do; the pattern's exponent field E gives floor(log2(max)) = E - 127 for a normal
+// maximum, so e = E - 135, which is at most 119, and every zero or subnormal maximum (E = 0)
+// falls to the clamp at -127.
 template <class E>
 struct MxEnc {
     uint32_t packed[E::VEC / 4];
@@ -568,7 +568,7 @@ struct RowsFor<E, true> { using type = MxRows<E>; };
 #endif
 
 // Waves per workgroup of prefill_slice_kernel: a tile is this many consecutive spans of one
-// column slice (the halo of each span after the first comes through LDS). Measured on MI355X
+// column slice (see SC_SLICE_LDS_HALO for where each span's halo comes from). Measured on MI355X
 // (varlen bf16 prefill, one process): 4 waves x 8-token spans 28.2 us; 8 x 4 33.6 us; 16 x 4
 // 35.2 us; 8 x 8 29.4 us; 2 x 8 28.8 us; 1 x 8 (each wave reading its own halo) 30.8 us. Shorter
 // spans keep fewer rows in flight per wave, and that costs more than the shorter tail of the grid
@@ -668,9 +668,9 @@ __global__ void __launch_bounds__(kSliceBlock, (slice_min_waves<W, MX>()))
         // slots (lane i: token i's slot; a span with no rows reads a stand-in word), the halo
         // (the R rows before the span, for wave 0 only when the others get theirs through LDS;
         // the stored state for a sequence's first span; otherwise R stand-in rows, discarded),
-        // the rows the next wave needs, then
-        // the other rows (past a short span's end the last row again; a span with no rows reads
-        // the stand-in). The stand-in is the taps array, at least W rows long.
+        // the rows the next wave needs, then the other rows (past a short span's end the last
+        // row again; a span with no rows reads the stand-in). The stand-in is the taps array, at
+        // least W rows long.
         const int last = n > 0 ? n - 1 : 0;
         const int64_t* sp = n > 0 ? a.slot + t0 + (wl < last ? wl : last)
                                   : reinterpret_cast<const int64_t*>(taps);
