@@ -41,9 +41,15 @@ namespace {
 
 constexpr int kBwdBlock = 256;
 constexpr int kBwdWaves = kBwdBlock / 64;
-// Tiles a workgroup walks: at most kMaxTilesPerGroup (bounds each fp32 partial's length), and
-// fewer when that leaves too few workgroups to fill the chip (kFillBlocks).
-constexpr int kMaxTilesPerGroup = 4;
+// Tiles a workgroup walks: as many as keep each lane's fp32 partial within kMaxPartialTokens
+// tokens of its span (the rounding bound of the parameter gradients assumes no more), and fewer
+// when that leaves too few workgroups to fill the chip (kFillBlocks); at most SC_BWD_MAX_TILES.
+// Measured on MI355X with 4 / up to 6 tiles (bf16, 10-token spans at W = 8, 12 at W = 4): the
+// long W = 8 backward 462 / 463 us, the mixed one 644 / 653 us.
+constexpr int kMaxPartialTokens = 64;
+#ifndef SC_BWD_MAX_TILES
+#define SC_BWD_MAX_TILES 4
+#endif
 #ifndef SC_BWD_FILL_BLOCKS
 #define SC_BWD_FILL_BLOCKS 2048
 #endif
@@ -225,6 +231,30 @@ constexpr int bwd_min_waves() {
     return PURE && W <= 4 && E::BYTES == 2 ? SC_BWD_WAVES_PURE : 2;
 }
 
+// Whether the tile's last wave loads the R rows after its span (for its phase 2) in its first
+// burst, with everything else; otherwise it loads them after the barrier, and the whole workgroup
+// waits for that round trip (measured on MI355X, bf16 W = 8, 131072 tokens: 530 us with the late
+// loads, 408 us with no phase-2 recompute at all). Early loads hold 2R more rows in registers:
+// every case but the ones where that spills (bf16 W = 8 over slices mixing K and V lanes, fp32
+// W = 8, fp32 W = 7 over mixed slices).
+#ifndef SC_BWD_PREFETCH_WIDE
+#define SC_BWD_PREFETCH_WIDE 1
+#endif
+// 1: a tile's last R input-gradient rows may be finished by the next tile of the same workgroup
+// (see `defer` in backward_kernel) instead of recomputing the next tile's first R tokens.
+#ifndef SC_BWD_DEFER
+#define SC_BWD_DEFER 1
+#endif
+template <class E, int W, bool PURE>
+constexpr bool bwd_prefetch_next() {
+    if (W <= 4) return true;
+    if (!SC_BWD_PREFETCH_WIDE) return false;
+    // with deferral (SC_BWD_DEFER) the bf16 W = 8 and fp32 W = 7 kernels over one-tensor slices
+    // have no registers left for the early loads
+    return E::BYTES == 2 ? (W < 8 || (PURE && !SC_BWD_DEFER))
+                         : (W <= 6 || (PURE && W == 7 && !SC_BWD_DEFER));
+}
+
 template <class E, int D, int W, int BT, bool PURE>
 __global__ void __launch_bounds__(kBwdBlock, (bwd_min_waves<E, W, PURE>())) backward_kernel(BwdArgs a) {
     using Q = Quad<E>;
@@ -237,9 +267,13 @@ __global__ void __launch_bounds__(kBwdBlock, (bwd_min_waves<E, W, PURE>())) back
     static_assert(BT >= R, "a wave's span must cover the window");
     // dc rows that wave w + 1 hands back to wave w (first R of its span), reused afterwards for
     // the workgroup's sum of the parameter-gradient partials.
-    constexpr bool kPrefetchNext = R <= 3;
+    constexpr bool kPrefetchNext = bwd_prefetch_next<E, W, PURE>();
+    constexpr bool kDefer = SC_BWD_DEFER && R > 0;
 
-    constexpr int kHand = NW * RR;
+    // LDS: the first R dc rows of each wave's span (NW * RR rows), then two buffers (by tile
+    // parity) for the last R dc rows of a tile's last span when it defers its last
+    // input-gradient rows to the next tile (2 * RR rows).
+    constexpr int kHand = NW * RR + 2 * RR;
     constexpr int kRed = (NW - 1) * (W + 1);
     __shared__ float4 lds[(kHand > kRed ? kHand : kRed) * 64];
 
@@ -289,6 +323,10 @@ __global__ void __launch_bounds__(kBwdBlock, (bwd_min_waves<E, W, PURE>())) back
         for (int k = 0; k < W; ++k) acc_t[k][v] = 0.0f;
     }
 
+    // The previous tile deferred its last R input-gradient rows (those at pending_t0 + BT - R ..)
+    // to this one.
+    bool pending = false;
+    int64_t pending_t0 = 0;
 #pragma unroll 1
     for (int gi = 0; gi < a.tiles_per_group; ++gi) {
         const int64_t tile = (int64_t)group * a.tiles_per_group + gi;
@@ -300,7 +338,10 @@ __global__ void __launch_bounds__(kBwdBlock, (bwd_min_waves<E, W, PURE>())) back
         const int64_t L = end - start;
         const int64_t j = tile - tile_base<BB>(a.cu, s, T);
         const int64_t ntiles = L > 0 ? (L + BB - 1) / BB : 1;
-        if (j < 0 || j >= ntiles) continue;  // the same for the whole workgroup
+        if (j < 0 || j >= ntiles) {  // the same for the whole workgroup
+            pending = false;  // (never set here: a deferring tile's successor is always walked)
+            continue;
+        }
 
         const int64_t p0 = j * BB + (int64_t)w * BT;  // span start, sequence position
         const int64_t t0 = start + p0;
@@ -308,6 +349,14 @@ __global__ void __launch_bounds__(kBwdBlock, (bwd_min_waves<E, W, PURE>())) back
         const int n = rem <= 0 ? 0 : (rem < BT ? (int)rem : BT);
         const int next_n = rem <= BT ? 0 : (rem - BT < R ? (int)(rem - BT) : R);
         const bool first_span = j == 0 && w == 0;
+        // Defer: when this workgroup walks the next tile too and the sequence continues into it,
+        // the tile's last wave does not recompute the next tile's first R tokens; it hands the dc
+        // of its own last R tokens to the next tile's wave 0 through LDS, which finishes the last
+        // R input-gradient rows of this tile from them and its own first R dc. Not when those rows
+        // carry the new-state loss. The same decision in every wave (uniform values only).
+        const int64_t p0_last = j * BB + (int64_t)(NW - 1) * BT;
+        const bool defer = kDefer && gi + 1 < a.tiles_per_group && tile + 1 < a.tiles &&
+                           L - p0_last > BT && !(gs != nullptr && p0_last + BT > L - R);
         int32_t idx = -1;
         bool from_state = false;
         if (j == 0) {
@@ -338,8 +387,8 @@ __global__ void __launch_bounds__(kBwdBlock, (bwd_min_waves<E, W, PURE>())) back
                 for (int m = 0; m < R; ++m) gsr[m] = Q::load(gs_seq + m * row_bytes + lane_off);
             }
             // the tile's last wave also fetches the R rows after its span now, for phase 2
-            // (narrow windows only: wide ones have no registers to spare)
-            if (kPrefetchNext && w == NW - 1 && next_n > 0) {
+            // (where the registers allow, see bwd_prefetch_next)
+            if (kPrefetchNext && w == NW - 1 && next_n > 0 && !defer) {
                 const int lastn = next_n - 1;
 #pragma unroll
                 for (int k = 0; k < R; ++k) {
@@ -449,7 +498,15 @@ __global__ void __launch_bounds__(kBwdBlock, (bwd_min_waves<E, W, PURE>())) back
             }
         }
         __syncthreads();
-        if (n > 0) {
+        if (n > 0 && defer && w == NW - 1) {
+            // ---- phase 2, deferring: hand the dc of the span's last R tokens to the next tile
+            // (two buffers by tile parity: wave 0 reads the previous tile's while this is written)
+#pragma unroll
+            for (int k = 0; k < R; ++k) {
+                const float* f = dcr[(BT - R + k) % W];
+                lds[((NW + (gi & 1)) * RR + k) * 64 + wl] = make_float4(f[0], f[1], f[2], f[3]);
+            }
+        } else if (n > 0) {
             // ---- phase 2: the last R rows of the span need dc of the R tokens after it ----
             float dcn[RR][4];  // dc of span tokens BT .. BT+R-1 (zero past the sequence)
 #pragma unroll
@@ -509,6 +566,39 @@ __global__ void __launch_bounds__(kBwdBlock, (bwd_min_waves<E, W, PURE>())) back
                         Q::store(dx + (t0 + q) * row_bytes + lane_off, Q::narrow(de));
                 }
             }
+            // The previous tile's deferred rows: row BT - R + m of its last span needs dc of
+            // its tokens BT + m - k, k = 0..W-1: this span's token m - k when m >= k (this
+            // wave's first R dc, left in LDS in phase 1), else the previous span's token
+            // BT + m - k (handed over by the previous tile's last wave).
+            if (kDefer && pending && w == 0) {
+                const int hb = NW + ((gi - 1) & 1);
+                float dn[RR][4], dp[RR][4];
+#pragma unroll
+                for (int k = 0; k < R; ++k) {
+                    const float4 f = lds[k * 64 + wl];
+                    dn[k][0] = f.x; dn[k][1] = f.y; dn[k][2] = f.z; dn[k][3] = f.w;
+                    const float4 g = lds[(hb * RR + k) * 64 + wl];
+                    dp[k][0] = g.x; dp[k][1] = g.y; dp[k][2] = g.z; dp[k][3] = g.w;
+                }
+#pragma unroll
+                for (int m = 0; m < R; ++m) {
+                    float de[4];
+#pragma unroll
+                    for (int k = 0; k < W; ++k) {
+                        const int tk = m - k;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const float dv = tk >= 0 ? dn[tk >= 0 ? tk : 0][v] : dp[tk >= 0 ? 0 : R + tk][v];
+                            de[v] = k == 0 ? tap[k][v] * dv : __builtin_fmaf(tap[k][v], dv, de[v]);
+                        }
+                    }
+                    const int64_t row = pending_t0 + BT - R + m;
+                    if constexpr (PURE)
+                        store_row<E>(dx, row, (uint32_t)row_bytes, true, lane_off, Q::narrow(de));
+                    else if (active)
+                        Q::store(dx + row * row_bytes + lane_off, Q::narrow(de));
+                }
+            }
         } else if (first_span && R > 0 && dstate != nullptr) {
             // an empty sequence: its new state is its initial window
 #pragma unroll
@@ -520,6 +610,8 @@ __global__ void __launch_bounds__(kBwdBlock, (bwd_min_waves<E, W, PURE>())) back
             }
         }
         __syncthreads();  // the hand-off rows are rewritten by the next tile
+        pending = defer;
+        pending_t0 = start + p0_last;
     }
 
     // ---- the workgroup's partial of the parameter gradients: waves summed in order ----
@@ -656,7 +748,9 @@ BwdShape backward_shape(int64_t total_tokens, int32_t num_seqs, int32_t num_head
     const int64_t bb = (int64_t)kBwdWaves * bt;
     sh.tiles = total_tokens / bb + num_seqs;
     int64_t per = sh.tiles * sh.slices / kFillBlocks;
-    per = per < 1 ? 1 : (per > kMaxTilesPerGroup ? kMaxTilesPerGroup : per);
+    int64_t max_per = kMaxPartialTokens / bt;
+    max_per = max_per < 1 ? 1 : (max_per > SC_BWD_MAX_TILES ? SC_BWD_MAX_TILES : max_per);
+    per = per < 1 ? 1 : (per > max_per ? max_per : per);
     sh.tiles_per_group = per;
     sh.groups = (sh.tiles + per - 1) / per;
     sh.chunks = (sh.groups + kChunk - 1) / kChunk;

@@ -197,6 +197,44 @@ def test_backward_reference_workload_shapes(name):
     print(f"{name} backward worst error/bound: {worst}")
 
 
+# Shapes large enough that each workgroup walks several consecutive tiles (tiles x column slices
+# at least 2 x 2048), so a tile's last input-gradient rows are finished by the next tile of the
+# same workgroup where the sequence continues into it, and recomputed where it does not (a
+# sequence boundary, the group's last tile, or rows that carry the new-state loss). Sequence
+# lengths put boundaries inside walked groups; every case has new-state losses.
+WALK = [
+    # dtype, H, D, W, lens: bf16 over one-tensor slices (W = 8: no early loads; W = 5: early
+    # loads; W = 4), bf16 and fp32 over slices mixing K and V lanes, fp32 over one-tensor slices
+    ("bf16", 8, 128, 8, [9000, 37, 6001, 0, 8100, 1, 913]),
+    ("bf16", 8, 128, 5, [20000, 3, 9001, 4100]),
+    ("bf16", 8, 128, 4, [12000, 9, 8001, 6200, 2]),
+    ("bf16", 3, 64, 7, [40000, 17, 30001, 15000]),
+    ("f32", 4, 64, 7, [33000, 5, 30001, 5000]),
+    ("f32", 3, 64, 6, [36000, 30001, 3]),
+]
+
+
+@pytest.mark.parametrize("dtype,H,D,W,lens", WALK,
+                         ids=[f"{s[0]}-H{s[1]}-D{s[2]}-W{s[3]}" for s in WALK])
+def test_backward_walking_several_tiles(dtype, H, D, W, lens):
+    from causal_short_convolution_amd import shortconv_kv_backward_workspace_size
+    hin = [1 if i % 2 == 0 else 0 for i in range(len(lens))]
+    case = BwdCase(dtype, H, D, W, lens, hin, seed=50 + W)
+    T, N = sum(lens), len(lens)
+    # the workspace holds one partial per (group, slice): fewer groups than tiles means the
+    # workgroups walk several tiles
+    lpt = H * D // 4
+    slices = (2 * lpt + 63) // 64
+    pure = lpt % 64 == 0
+    bt = (12 if pure and W <= 4 else 16 if W <= 5 else 10) if dtype == "bf16" else \
+        (16 if W <= 1 else 8)
+    tiles = T // (4 * bt) + N
+    partial = slices * (W + 1) * 256 * 4
+    size = shortconv_kv_backward_workspace_size(T, N, H, D, W, TORCH_DT[dtype])
+    assert size < 0.75 * tiles * partial, "the workgroups walk one tile each"
+    case.check()
+
+
 def test_backward_without_sequences_zeroes_parameter_gradients():
     H, D, W = 2, 64, 4
     dkt = torch.full((W, H, D), float("nan"), device=DEV)
