@@ -215,10 +215,10 @@ def test_backward_workspace_size(lib):
     _binding.load_library()  # sets the ctypes signatures
     size = lib.shortconv_kv_backward_workspace_size
     # bf16, H=8, D=128, W=4: 256 lanes per tensor -> 8 slices of 64, each holding one tensor, so
-    # tiles of 4 waves x 12 tokens: 17060 // 48 + 8 = 363 tiles; 363 * 8 slices < 2 * 2048 -> 1
-    # tile per group, 363 groups; an fp32 partial of (W + 1) * 64 lanes * 4 channels per slice and
-    # group, then fp64 sums of chunks of 64 groups (6 chunks)
-    assert size(17060, 8, 8, 128, 4, 1) == 363 * 8 * 5 * 256 * 4 + 6 * 8 * 5 * 256 * 8
+    # tiles of 4 waves x 12 tokens: 17060 // 48 + 8 = 363 tiles; 363 * 8 slices // 1024 = 2
+    # tiles per group, 182 groups; an fp32 partial of (W + 1) * 64 lanes * 4 channels per slice
+    # and group, then fp64 sums of chunks of 64 groups (3 chunks)
+    assert size(17060, 8, 8, 128, 4, 1) == 182 * 8 * 5 * 256 * 4 + 3 * 8 * 5 * 256 * 8
     # the long prefill (W=8 -> 10-token spans): 131072 // 40 + 1 = 3277 tiles, 4 per group
     assert size(131072, 1, 8, 128, 8, 1) == 820 * 8 * 9 * 256 * 4 + 13 * 8 * 9 * 256 * 8
     assert size(0, 0, 8, 128, 4, 1) == 0
