@@ -27,8 +27,10 @@
 //            gradient of every token whose dc window (the token and the W-1 after it) lies inside
 //            the span; its first W-1 dc rows go to LDS;
 //   phase 2: after a barrier, emits the input gradient of its last W-1 tokens from the next
-//            wave's first dc rows (LDS), or, for the tile's last wave, from W-1 tokens of the
-//            next tile that it recomputes.
+//            wave's first dc rows (LDS). The tile's last wave needs the next tile's first W-1 dc:
+//            when the workgroup walks that tile next, it hands its own last W-1 dc rows through
+//            LDS to that tile's wave 0, which finishes those rows in its own phase 2; otherwise it
+//            recomputes the next tile's first W-1 tokens.
 // The first wave of a sequence's first tile also writes the initial-window gradient.
 // The parameter gradients leave each workgroup as one partial (the 4 waves summed through LDS,
 // in wave order) in a workspace; further kernels add the partials in fp64 in a fixed order (by
