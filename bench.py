@@ -729,13 +729,11 @@ def summarize_profile(dirs):
             factors[ctr] = known_kib / (sum(copies) / len(copies))
             out.append(f"calibration copy {ctr}: {sum(copies) / len(copies):.1f} KiB per dispatch "
                        f"for {known_kib:.0f} KiB moved -> factor {factors[ctr]:.4f}")
-    dram = {}
     for ctr, size in (("TCC_EA0_RDREQ_DRAM_sum", DRAM_RD_BYTES),
                       ("TCC_EA0_WRREQ_DRAM_sum", DRAM_WR_BYTES)):
         copies = sorted(per.get(("copy", ctr), []))[-5:]
         if copies:
             mean = sum(copies) / len(copies)
-            dram[ctr] = size
             out.append(f"calibration copy {ctr}: {mean:.0f} requests per dispatch x {size} B = "
                        f"{mean * size / COPY_BYTES:.4f} x the {COPY_BYTES} bytes moved")
 
