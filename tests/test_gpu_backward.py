@@ -235,6 +235,33 @@ def test_backward_walking_several_tiles(dtype, H, D, W, lens):
     case.check()
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_backward_walking_several_tiles_random(seed):
+    """Seeded random shapes (dtype, heads, head_dim, width, packing, resumed sequences, new-state
+    losses) sized so that each workgroup walks at least two tiles."""
+    from causal_short_convolution_amd import shortconv_kv_backward_workspace_size
+    rng = np.random.default_rng(300 + seed)
+    dtype = ("bf16", "f32")[int(rng.integers(2))]
+    H, D = [(8, 128), (4, 64), (3, 64), (2, 128), (6, 64), (16, 64), (1, 256)][rng.integers(7)]
+    W = int(rng.integers(2, 9))
+    lpt = H * D // 4
+    slices = (2 * lpt + 63) // 64
+    pure = lpt % 64 == 0
+    bt = (12 if pure and W <= 4 else 16 if W <= 5 else 10) if dtype == "bf16" else 8
+    T = (2 * 1024 // slices + 1) * 4 * bt + int(rng.integers(0, 4 * bt * 40))
+    cuts = np.sort(rng.integers(0, T, size=int(rng.integers(0, 8))))
+    lens = np.diff(np.concatenate([[0], cuts, [T]])).tolist()
+    if rng.random() < 0.3:
+        lens.insert(int(rng.integers(len(lens))), 0)
+    hin = [int(x) for x in rng.integers(0, 2, size=len(lens))]
+    tiles = sum(lens) // (4 * bt) + len(lens)
+    size = shortconv_kv_backward_workspace_size(sum(lens), len(lens), H, D, W, TORCH_DT[dtype])
+    assert size < 0.75 * tiles * slices * (W + 1) * 1024, "the workgroups walk one tile each"
+    case = BwdCase(dtype, H, D, W, lens, hin, seed=int(rng.integers(1 << 30)),
+                   gs=bool(rng.random() < 0.7))
+    case.check()
+
+
 def test_backward_without_sequences_zeroes_parameter_gradients():
     H, D, W = 2, 64, 4
     dkt = torch.full((W, H, D), float("nan"), device=DEV)
