@@ -706,8 +706,9 @@ def summarize_profile(dirs):
                 out.append(f"  {name[:56]:56s} grid={grid:>11s} n={len(v):>5d} "
                            f"mean_ns={sum(v) / len(v):10.1f} p10_ns={q(0.1):>8d} "
                            f"median_ns={q(0.5):>8d} p90_ns={q(0.9):>8d}")
-            out.append("kernel resources as the tracer reports them (VGPR_Count in its own units: half "
-                       "the assembler's .vgpr_count on this build; LDS and scratch bytes):")
+            out.append("kernel resources as the tracer reports them (VGPR_Count in its own units, not "
+                       "the register allocation, which the compiler's resource report gives; LDS and "
+                       "scratch bytes):")
             for name, (vg, lds, scr) in sorted(res.items()):
                 if any(k in name for k in KERNELS):
                     out.append(f"  {name[:56]:56s} vgpr={vg} lds={lds} scratch={scr}")

@@ -46,8 +46,8 @@ constexpr int kBwdWaves = kBwdBlock / 64;
 // Tiles a workgroup walks: as many as keep each lane's fp32 partial within kMaxPartialTokens
 // tokens of its span (the rounding bound of the parameter gradients assumes no more), and fewer
 // when that leaves too few workgroups to fill the chip (kFillBlocks); at most SC_BWD_MAX_TILES.
-// Measured on MI355X with 4 / up to 6 tiles (bf16, 10-token spans at W = 8, 12 at W = 4): the
-// long W = 8 backward 462 / 463 us, the mixed one 644 / 653 us.
+// Measured on MI355X with 4 / up to 6 tiles (bf16, 12-token spans at W = 4): the mixed W = 4
+// backward 644 / 653 us (and, with the 10-token spans W = 8 had then, the long one 462 / 463 us).
 constexpr int kMaxPartialTokens = 64;
 #ifndef SC_BWD_MAX_TILES
 #define SC_BWD_MAX_TILES 4
@@ -78,11 +78,20 @@ constexpr int64_t kFillBlocks = SC_BWD_FILL_BLOCKS;
 #ifndef SC_BWD_BT_BF16_PURE
 #define SC_BWD_BT_BF16_PURE 12  // bf16, W <= 4, single-tensor slices (3 waves per SIMD)
 #endif
+// bf16, W > 5, single-tensor slices: the register count stays at ~242 (2 waves per SIMD) from
+// 8 to 20 tokens here, so longer spans only shed halo rows, recomputed rows and partials.
+// Measured on MI355X (W = 8, 131 072 tokens, one process, spans of 10 / 12 / 14 / 16 / 20):
+// 461.7 / 447.8 / 438.9 / 424.1 / 423.8 us per backward; 24 spills.
+#ifndef SC_BWD_BT_BF16_WIDE_PURE
+#define SC_BWD_BT_BF16_WIDE_PURE 16
+#endif
 template <class E, int W, bool PURE = false>
 constexpr int bwd_span() {
-    return E::BYTES == 2 ? (PURE && W <= 4 ? SC_BWD_BT_BF16_PURE
-                                           : (W <= 5 ? SC_BWD_BT_BF16 : SC_BWD_BT_BF16_WIDE))
-                         : (W <= 1 ? SC_BWD_BT_F32 : SC_BWD_BT_F32_WIDE);
+    return E::BYTES == 2
+               ? (PURE && W <= 4 ? SC_BWD_BT_BF16_PURE
+                                 : (W <= 5 ? SC_BWD_BT_BF16
+                                           : (PURE ? SC_BWD_BT_BF16_WIDE_PURE : SC_BWD_BT_BF16_WIDE)))
+               : (W <= 1 ? SC_BWD_BT_F32 : SC_BWD_BT_F32_WIDE);
 }
 
 // 4 channels of one lane, in the I/O element type, with streaming (non-temporal) access.
@@ -748,6 +757,7 @@ BwdShape backward_shape(int64_t total_tokens, int32_t num_seqs, int32_t num_head
     const bool pure = sh.lanes_per_tensor % 64 == 0;  // the kernel launch_backward picks
     const int bt = dtype == 1 ? (pure && width <= 4 ? bwd_span<BF16, 1, true>()
                                  : width <= 5       ? bwd_span<BF16, 1>()
+                                 : pure             ? bwd_span<BF16, 8, true>()
                                                     : bwd_span<BF16, 8>())
                               : (width <= 1 ? bwd_span<F32, 1>() : bwd_span<F32, 8>());
     const int64_t bb = (int64_t)kBwdWaves * bt;

@@ -219,8 +219,9 @@ def test_backward_workspace_size(lib):
     # tiles per group, 182 groups; an fp32 partial of (W + 1) * 64 lanes * 4 channels per slice
     # and group, then fp64 sums of chunks of 64 groups (3 chunks)
     assert size(17060, 8, 8, 128, 4, 1) == 182 * 8 * 5 * 256 * 4 + 3 * 8 * 5 * 256 * 8
-    # the long prefill (W=8 -> 10-token spans): 131072 // 40 + 1 = 3277 tiles, 4 per group
-    assert size(131072, 1, 8, 128, 8, 1) == 820 * 8 * 9 * 256 * 4 + 13 * 8 * 9 * 256 * 8
+    # the long prefill (W=8 over one-tensor slices -> 16-token spans): 131072 // 64 + 1 = 2049
+    # tiles, 4 per group (64 tokens per lane), 513 groups, 9 chunks
+    assert size(131072, 1, 8, 128, 8, 1) == 513 * 8 * 9 * 256 * 4 + 9 * 8 * 9 * 256 * 8
     assert size(0, 0, 8, 128, 4, 1) == 0
     assert size(10, 2, 8, 96, 4, 1) == 2 ** 64 - 1  # unsupported head_dim -> SIZE_MAX
     assert "head_dim" in lib.shortconv_last_error().decode()

@@ -226,7 +226,7 @@ def test_backward_walking_several_tiles(dtype, H, D, W, lens):
     lpt = H * D // 4
     slices = (2 * lpt + 63) // 64
     pure = lpt % 64 == 0
-    bt = (12 if pure and W <= 4 else 16 if W <= 5 else 10) if dtype == "bf16" else \
+    bt = (12 if pure and W <= 4 else 16 if W <= 5 or pure else 10) if dtype == "bf16" else \
         (16 if W <= 1 else 8)
     tiles = T // (4 * bt) + N
     partial = slices * (W + 1) * 256 * 4
@@ -247,7 +247,7 @@ def test_backward_walking_several_tiles_random(seed):
     lpt = H * D // 4
     slices = (2 * lpt + 63) // 64
     pure = lpt % 64 == 0
-    bt = (12 if pure and W <= 4 else 16 if W <= 5 else 10) if dtype == "bf16" else 8
+    bt = (12 if pure and W <= 4 else 16 if W <= 5 or pure else 10) if dtype == "bf16" else 8
     T = (2 * 1024 // slices + 1) * 4 * bt + int(rng.integers(0, 4 * bt * 40))
     cuts = np.sort(rng.integers(0, T, size=int(rng.integers(0, 8))))
     lens = np.diff(np.concatenate([[0], cuts, [T]])).tolist()
