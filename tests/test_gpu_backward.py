@@ -203,9 +203,11 @@ def test_backward_reference_workload_shapes(name):
 # sequence boundary, the group's last tile, or rows that carry the new-state loss). Sequence
 # lengths put boundaries inside walked groups; every case has new-state losses.
 WALK = [
-    # dtype, H, D, W, lens: bf16 over one-tensor slices (W = 8: no early loads; W = 5: early
-    # loads; W = 4), bf16 and fp32 over slices mixing K and V lanes, fp32 over one-tensor slices
+    # dtype, H, D, W, lens: bf16 over one-tensor slices (W = 8: no early loads; W = 6: 16-token
+    # spans with early loads; W = 5: early loads; W = 4), bf16 and fp32 over slices mixing K and V
+    # lanes, fp32 over one-tensor slices
     ("bf16", 8, 128, 8, [9000, 37, 6001, 0, 8100, 1, 913]),
+    ("bf16", 4, 128, 6, [20000, 7, 15001, 3000]),
     ("bf16", 8, 128, 5, [20000, 3, 9001, 4100]),
     ("bf16", 8, 128, 4, [12000, 9, 8001, 6200, 2]),
     ("bf16", 3, 64, 7, [40000, 17, 30001, 15000]),
