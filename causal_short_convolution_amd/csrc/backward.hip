@@ -283,6 +283,14 @@ __global__ void __launch_bounds__(kBwdBlock, (bwd_min_waves<E, W, PURE>())) back
     // the workgroup's sum of the parameter-gradient partials.
     constexpr bool kPrefetchNext = bwd_prefetch_next<E, W, PURE>();
     constexpr bool kDefer = SC_BWD_DEFER && R > 0;
+    // Row byte offsets (wave-uniform). For W <= 4 they are kept scalar through readfirstlane, so
+    // each row address is one add to the lane's base rather than a quarter-rate 64-bit
+    // multiply-add on the vector unit. Measured on MI355X (bf16, same process): varlen 61.5 ->
+    // 61.0 us, mixed 650.7 -> 642.4 us; at W = 8 (431 against 427 us) it is left to the compiler.
+    const auto roff = [](int64_t v) -> int64_t {
+        if constexpr (W <= 4) return uniform(v);
+        else return v;
+    };
 
     // LDS: the first R dc rows of each wave's span (NW * RR rows), then two buffers (by tile
     // parity) for the last R dc rows of a tile's last span when it defers its last
@@ -398,7 +406,7 @@ __global__ void __launch_bounds__(kBwdBlock, (bwd_min_waves<E, W, PURE>())) back
             Raw halo[RR], xr[BT], gr[BT];
             if (has_tail) {
 #pragma unroll
-                for (int m = 0; m < R; ++m) gsr[m] = Q::load(gs_seq + m * row_bytes + lane_off);
+                for (int m = 0; m < R; ++m) gsr[m] = Q::load(gs_seq + roff(m * row_bytes) + lane_off);
             }
             // the tile's last wave also fetches the R rows after its span now, for phase 2
             // (where the registers allow, see bwd_prefetch_next)
@@ -407,21 +415,21 @@ __global__ void __launch_bounds__(kBwdBlock, (bwd_min_waves<E, W, PURE>())) back
 #pragma unroll
                 for (int k = 0; k < R; ++k) {
                     const int r = k < lastn ? k : lastn;
-                    xn[k] = Q::load(x + (t0 + BT + r) * xs + lane_off);
-                    gn[k] = Q::load(dy + (t0 + BT + r) * row_bytes + lane_off);
+                    xn[k] = Q::load(x + roff((t0 + BT + r) * xs) + lane_off);
+                    gn[k] = Q::load(dy + roff((t0 + BT + r) * row_bytes) + lane_off);
                 }
             }
             // The halo and the span's last R input rows are loaded without the streaming hint,
             // the other rows with it, the mix that measured fastest (as in the forward).
 #pragma unroll
-            for (int k = 0; k < R; ++k) halo[k] = Q::load_keep(hsrc + k * hstride + lane_off);
+            for (int k = 0; k < R; ++k) halo[k] = Q::load_keep(hsrc + roff(k * hstride) + lane_off);
             const int last = n - 1;
 #pragma unroll
             for (int i = 0; i < BT; ++i) {
                 const int r = i < last ? i : last;
-                xr[i] = i >= BT - R ? Q::load_keep(x + (t0 + r) * xs + lane_off)
-                                    : Q::load(x + (t0 + r) * xs + lane_off);
-                gr[i] = Q::load(dy + (t0 + r) * row_bytes + lane_off);
+                xr[i] = i >= BT - R ? Q::load_keep(x + roff((t0 + r) * xs) + lane_off)
+                                    : Q::load(x + roff((t0 + r) * xs) + lane_off);
+                gr[i] = Q::load(dy + roff((t0 + r) * row_bytes) + lane_off);
             }
             if (first_span && !from_state) {
 #pragma unroll
@@ -542,8 +550,8 @@ __global__ void __launch_bounds__(kBwdBlock, (bwd_min_waves<E, W, PURE>())) back
 #pragma unroll
                         for (int k = 0; k < R; ++k) {
                             const int r = k < lastn ? k : lastn;
-                            xn[k] = Q::load(x + (t0 + BT + r) * xs + lane_off);
-                            gn[k] = Q::load(dy + (t0 + BT + r) * row_bytes + lane_off);
+                            xn[k] = Q::load(x + roff((t0 + BT + r) * xs) + lane_off);
+                            gn[k] = Q::load(dy + roff((t0 + BT + r) * row_bytes) + lane_off);
                         }
                     }
 #pragma unroll
@@ -618,7 +626,7 @@ __global__ void __launch_bounds__(kBwdBlock, (bwd_min_waves<E, W, PURE>())) back
 #pragma unroll
             for (int m = 0; m < R; ++m) {
                 float de[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                if (gs != nullptr && from_state) Q::widen(Q::load(gs_seq + m * row_bytes + lane_off), de);
+                if (gs != nullptr && from_state) Q::widen(Q::load(gs_seq + roff(m * row_bytes) + lane_off), de);
                 if (active)
                     Q::store(dstate + ((int64_t)s * R + m) * row_bytes + lane_off, Q::narrow(de));
             }

@@ -176,8 +176,12 @@ struct PlainSink {
     // the pool).
     using Enc = uint4;
     __device__ Enc encode(const float (&o)[E::VEC]) const { return E::narrow(o); }
+    // The slot is wave-uniform in every caller; its byte offset is kept scalar (read through
+    // readfirstlane), so the address is one add to the lane's base instead of a 64-bit
+    // multiply-add on the vector unit at quarter rate.
     __device__ void write(int64_t slot, bool active, const Enc& out) const {
-        if (active && slot >= 0 && slot < num_slots) strow(cache + slot * row_bytes, lane_off, out);
+        if (active && slot >= 0 && slot < num_slots)
+            strow(cache + uniform(slot * row_bytes), lane_off, out);
     }
     __device__ void put(int64_t slot, bool active, const float (&o)[E::VEC]) const {
         write(slot, active, encode(o));
@@ -265,7 +269,7 @@ struct MxSink {
     __device__ Enc encode(const float (&o)[VEC]) const { return mx_encode<E>(o); }
     __device__ void write(int64_t slot, bool active, const Enc& enc) const {
         if (!(active && slot >= 0 && slot < num_slots)) return;
-        char* row = codes + slot * row_elems + code_off;
+        char* row = codes + uniform(slot * row_elems) + code_off;  // (offset kept scalar)
         if (VEC == 8) {
             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
             const u32x2 w = {enc.packed[0], enc.packed[VEC / 4 - 1]};
@@ -274,7 +278,7 @@ struct MxSink {
             __builtin_nontemporal_store(enc.packed[0], reinterpret_cast<uint32_t*>(row));
         }
         if (scale_lane)
-            *reinterpret_cast<uint8_t*>(scales + slot * (row_elems / 32) + scale_off) =
+            *reinterpret_cast<uint8_t*>(scales + uniform(slot * (row_elems / 32)) + scale_off) =
                 (uint8_t)(enc.e + 127);
     }
     __device__ void put(int64_t slot, bool active, const float (&o)[VEC]) const {
@@ -290,7 +294,13 @@ struct SinkFor<E, true> { using type = MxSink<E>; };
 // ------------------------------------------------------------------------------------------------
 // Prefill
 // ------------------------------------------------------------------------------------------------
-template <class E, int D, int W, int BT, bool MX>
+// PURE: every 64-lane slice holds one tensor (H * D a multiple of 256 elements of each of K and
+// V), so every lane is active and the tensor, with every base address picked by it, is
+// wave-uniform: row and cache addresses are then a scalar base plus the lane's 32-bit offset
+// (fewer 64-bit multiply-adds on the vector unit, at quarter rate). Measured on MI355X (W = 8,
+// 131 072 tokens, same process): bf16 rows 169.2 -> 168.4 us, MXFP8 rows 179.2 -> 177.4 us,
+// outputs bit-identical.
+template <class E, int D, int W, int BT, bool MX, bool PURE>
 __global__ void __launch_bounds__(kBlock, (span_min_waves<W, MX>())) prefill_kernel(StepArgs a) {
     constexpr int VEC = E::VEC;
     constexpr int LPH = D / VEC;
@@ -321,9 +331,10 @@ __global__ void __launch_bounds__(kBlock, (span_min_waves<W, MX>())) prefill_ker
     const int slice = unit - tile * slices;
     const int lane = slice * 64 + wl;
     // idle lanes load lane 0's column and store nothing
-    const bool active = lane < 2 * a.lanes_per_tensor;
+    const bool active = PURE || lane < 2 * a.lanes_per_tensor;
     const int ln = active ? lane : 0;
-    const int tensor = ln >= a.lanes_per_tensor;
+    const int tensor = PURE ? uniform(slice * 64 >= a.lanes_per_tensor ? 1 : 0)
+                            : (ln >= a.lanes_per_tensor ? 1 : 0);
     const int c = ln - tensor * a.lanes_per_tensor;
     const int h = c / LPH;
     const int d0 = (c - h * LPH) * VEC;
@@ -382,7 +393,7 @@ __global__ void __launch_bounds__(kBlock, (span_min_waves<W, MX>())) prefill_ker
                                             : reinterpret_cast<const char*>(pick(a.taps, tensor));
             const int64_t hstride = j > 0 ? stride_bytes : row_bytes;
 #pragma unroll
-            for (int k = 0; k < R; ++k) halo[k] = ldrow_keep(hsrc + k * hstride, lane_off);
+            for (int k = 0; k < R; ++k) halo[k] = ldrow_keep(hsrc + uniform(k * hstride), lane_off);
         }
         // Past a short span's end the last row is read again (and not used). Lane l < BT loads
         // token l's cache slot (one vector load instead of BT scalar ones, which the compiler
@@ -392,12 +403,13 @@ __global__ void __launch_bounds__(kBlock, (span_min_waves<W, MX>())) prefill_ker
         // without the streaming hint, the others with it: measured on MI355X, this mix is faster
         // than all streaming (varlen bf16 prefill 30.3 -> 28.1 us) or none, with unchanged HBM
         // reads in the counters; why it is faster is not established.
+        // (row offsets kept scalar, as in the sinks)
 #pragma unroll
         for (int i = BT - R; i < BT; ++i)
-            raw[i] = ldrow_keep(xb + (i < last ? i : last) * stride_bytes, lane_off);
+            raw[i] = ldrow_keep(xb + uniform((i < last ? i : last) * stride_bytes), lane_off);
 #pragma unroll
         for (int i = 0; i < BT - R; ++i)
-            raw[i] = ldrow(xb + (i < last ? i : last) * stride_bytes, lane_off);
+            raw[i] = ldrow(xb + uniform((i < last ? i : last) * stride_bytes), lane_off);
         lane_slot = a.slot[t0 + (wl < last ? wl : last)];
     }
     // LDS-staged halo: wave w hands its last R rows to wave w + 1, so a row is fetched once.
@@ -968,9 +980,13 @@ __global__ void __launch_bounds__(kBlock) mx_quantize_kernel(StepArgs a) {
 using KernelFn = void (*)(StepArgs);
 
 template <class E, int D, int W>
-constexpr KernelFn prefill_fn() { return prefill_kernel<E, D, W, span_tokens<W, false>(), false>; }
+constexpr KernelFn prefill_fn() {
+    return prefill_kernel<E, D, W, span_tokens<W, false>(), false, false>;
+}
 template <class E, int D, int W>
-constexpr KernelFn prefill_mx_fn() { return prefill_kernel<E, D, W, span_tokens<W, true>(), true>; }
+constexpr KernelFn prefill_mx_fn() {
+    return prefill_kernel<E, D, W, span_tokens<W, true>(), true, false>;
+}
 #ifndef SC_SLICE_BT
 #define SC_SLICE_BT 8
 #endif
@@ -983,11 +999,11 @@ constexpr KernelFn prefill_mx_fn() { return prefill_kernel<E, D, W, span_tokens<
 #ifndef SC_SLICE_BT_WIDE_MX
 #define SC_SLICE_BT_WIDE_MX 8
 #endif
-// Widest window served by prefill_slice_kernel; wider ones use prefill_kernel. Measured on
-// MI355X (bf16, W = 8, 131072 tokens, 8 x 128 heads, one process): prefill_kernel (16-token
-// spans held until every row is in, 2 waves per SIMD) 172.8 us; prefill_slice_kernel at 2 waves
-// per SIMD with 16-token spans 179.8 us, with 8-token spans 223.8 us (at 3 waves per SIMD its
-// registers spill). MXFP8 rows: 185.4 / 186.4 / 219.8 us.
+// Widest window served by prefill_slice_kernel; wider ones over one-tensor slices use
+// prefill_kernel's PURE form. Measured on MI355X (bf16, W = 8, 131072 tokens, 8 x 128 heads, one
+// process): prefill_kernel (16-token spans held until every row is in, 2 waves per SIMD)
+// 172.8 us; prefill_slice_kernel at 2 waves per SIMD with 16-token spans 179.8 us, with 8-token
+// spans 223.8 us (at 3 waves per SIMD its registers spill). MXFP8 rows: 185.4 / 186.4 / 219.8 us.
 #ifndef SC_SLICE_MAX_W
 #define SC_SLICE_MAX_W 4
 #endif
@@ -995,17 +1011,19 @@ template <int W, bool MX>
 constexpr int slice_span_tokens() {
     return W <= 4 ? (MX ? SC_SLICE_BT_MX : SC_SLICE_BT) : (MX ? SC_SLICE_BT_WIDE_MX : SC_SLICE_BT_WIDE);
 }
+// Prefill over one-tensor slices: prefill_slice_kernel up to SC_SLICE_MAX_W, then prefill_kernel
+// in its PURE form.
 template <class E, int D, int W>
 constexpr KernelFn prefill_slice_fn() {
     if constexpr (W <= SC_SLICE_MAX_W)
         return prefill_slice_kernel<E, D, W, slice_span_tokens<W, false>(), false>;
-    else return prefill_kernel<E, D, W, span_tokens<W, false>(), false>;
+    else return prefill_kernel<E, D, W, span_tokens<W, false>(), false, true>;
 }
 template <class E, int D, int W>
 constexpr KernelFn prefill_slice_mx_fn() {
     if constexpr (W <= SC_SLICE_MAX_W)
         return prefill_slice_kernel<E, D, W, slice_span_tokens<W, true>(), true>;
-    else return prefill_kernel<E, D, W, span_tokens<W, true>(), true>;
+    else return prefill_kernel<E, D, W, span_tokens<W, true>(), true, true>;
 }
 template <class E, int D, int W>
 constexpr KernelFn decode_fn() { return decode_kernel<E, D, W, false>; }
@@ -1099,7 +1117,10 @@ hipError_t launch_prefill(StepArgs a, int dtype, int head_dim, int width, bool m
         hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(kSliceBlock), 0, stream, a);
         return hipGetLastError();
     }
-    const KernelFn k = (mx ? kPrefillMx : kPrefill)[dtype][d_index(head_dim)][width - 1];
+    // one-tensor slices (wider windows): prefill_kernel's PURE form; other shapes: the general one
+    const bool pure = a.lanes_per_tensor % 64 == 0;
+    const KernelFn k = (pure ? (mx ? kPrefillSliceMx : kPrefillSlice) : (mx ? kPrefillMx : kPrefill))
+        [dtype][d_index(head_dim)][width - 1];
     hipLaunchKernelGGL(k, dim3((unsigned)units), dim3(kBlock), 0, stream, a);
     return hipGetLastError();
 }
