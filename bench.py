@@ -46,6 +46,8 @@ sys.path.insert(0, ROOT)
 METRIC = "fused ShortConv K/V tokens/s + achieved HBM GB/s (% of 8 TB/s), prefill & decode"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
 MALL_BYTES = 256 << 20          # MI355X Infinity Cache
+COLD_FLUSH_BYTES = 2 * MALL_BYTES  # scratch written before every cold launch
+COLD_LAUNCHES = 60
 KERNEL_SRC = [os.path.join(ROOT, "causal_short_convolution_amd", "csrc", f)
               for f in ("kernels.hip", "device_common.h")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_kernels_traffic.md")
@@ -146,13 +148,16 @@ def parse():
                     help="measure the headline workload only (no other workloads, MXFP8 rows, "
                          "speculative verify or backward)")
     ap.add_argument("--only", default=None,
-                    choices=["main", "decode", "mxfp8", "verify", "backward", "copy", "pattern"],
+                    choices=["main", "decode", "mxfp8", "verify", "backward", "copy", "pattern",
+                             "cold"],
                     help="run one measurement only (for profiling); prints no JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a graph")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--cold-flush", default="write", choices=["write", "read"],
+                    help="how --only cold evicts the caches before each launch")
     ap.add_argument("--summarize-profile", default=None, nargs="+", metavar="DIR")
     return ap.parse_args()
 
@@ -762,6 +767,50 @@ def summarize_profile(dirs):
 
 
 # ------------------------------------------------------------------------------------------------
+def measure_cold(torch, w, launches=COLD_LAUNCHES, warmup=3, flush="write"):
+    """The cold protocol: before every timed step a 512 MiB scratch write (twice the Infinity
+    Cache) evicts the step's data from every cache; each step is then timed alone, eagerly, by HIP
+    events on its stream (the interval includes the launch's own dispatch latency, which a graph
+    replay hides), and the median over the launches is reported with p10 and p90. A kernel trace
+    of `--only cold` gives the same launches' kernel durations. flush="read" reads the scratch
+    instead, which evicts as much but leaves no dirty lines for the step to write back."""
+    alg = sum(algorithmic_bytes(w, st) for st in w.steps)
+    reps = device_replicas(w, torch, 1)
+    step = launcher(w, reps[0])
+    scratch = torch.empty(COLD_FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    words = scratch.view(torch.int32)
+    for i in range(warmup + launches):
+        if flush == "read":
+            torch.amax(words)
+        else:
+            scratch.fill_(i & 0xFF)
+        if i >= warmup:
+            evs[i - warmup][0].record()
+        step()
+        if i >= warmup:
+            evs[i - warmup][1].record()
+    torch.cuda.synchronize()
+    us = sorted(1e3 * a.elapsed_time(b) for a, b in evs)
+    del reps, scratch
+
+    def q(f):
+        return us[min(len(us) - 1, int(f * len(us)))]
+    med = q(0.5)
+    return {"launches": launches, "flush": flush, "flush_bytes": COLD_FLUSH_BYTES, "median_us": med,
+            "p10_us": q(0.1), "p90_us": q(0.9), "achieved_GBps": alg / (med * 1e-6) / 1e9,
+            "frac_of_hbm_peak": alg / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "timing": "eager launch between HIP events, after a cache-evicting scratch " +
+                      ("read" if flush == "read" else "write")}
+
+
+def cold_pair(torch, w):
+    """The cold protocol with both flushes: the scratch written (as the protocol states) and read
+    (the same eviction, with no dirty lines left in the caches)."""
+    return {f"{fl}_flush": _round(measure_cold(torch, w, flush=fl)) for fl in ("write", "read")}
+
+
 def config_measure(torch, name, args, graph, cache="io"):
     """The fused step on workload `name` (every call of one step, in order), with the same-bytes
     copy ceiling. Returns (workload, entry)."""
@@ -836,6 +885,9 @@ def main():
             m = pattern_ceiling(torch, w, args.steps, args.warmup)
             m["achieved_GBps"] = m["GBps"]
             print(json.dumps(m["forms"]), flush=True)
+        elif args.only == "cold":
+            m = measure_cold(torch, w, flush=args.cold_flush)
+            m["kernel_us_mean"] = m["median_us"]  # (the median, for the line below)
         else:
             m = measure_verify(torch, args.steps, args.warmup, args.seed, graph)
         print(f"bench.py: {args.only}: {m['kernel_us_mean']:.2f} us per step, "
@@ -849,6 +901,9 @@ def main():
 
     progress(f"{n}: fused step")
     main_m = measure(torch, w, args.steps, args.warmup, reseed_main, graph)
+    progress(f"{n}: cold launches")
+    cold = cold_pair(torch, w)
+    free_device(torch)
     extra = {}
     others = [] if args.no_extras else [c for c in workloads.CONFIG_NAMES if c != n]
     if args.no_decode and "decode" in others:
@@ -857,6 +912,9 @@ def main():
     for name in others:
         progress(f"{name}: fused step")
         wc, entry = config_measure(torch, name, args, graph)
+        free_device(torch)
+        progress(f"{name}: cold launches")
+        entry["cold_protocol"] = cold_pair(torch, wc)
         free_device(torch)
         if name in big:
             progress(f"{name}: MXFP8 cache rows")
@@ -953,6 +1011,7 @@ def main():
                          "kernel_over_copy": main_m["achieved_GBps"] / ceil["GBps"],
                          "forms": ceil["forms"]},
         **({"pattern_ceiling": pattern} if pattern else {}),
+        "cold_protocol": cold,
         **extra,
     }
     if not args.no_cpu_baseline:
