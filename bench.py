@@ -156,6 +156,8 @@ def parse():
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--eager", action="store_true", help="launch from Python instead of a graph")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-launch legs (e.g. under a kernel trace of the warm steps)")
     ap.add_argument("--cold-flush", default="write", choices=["write", "read"],
                     help="how --only cold evicts the caches before each launch")
     ap.add_argument("--summarize-profile", default=None, nargs="+", metavar="DIR")
@@ -901,9 +903,11 @@ def main():
 
     progress(f"{n}: fused step")
     main_m = measure(torch, w, args.steps, args.warmup, reseed_main, graph)
-    progress(f"{n}: cold launches")
-    cold = cold_pair(torch, w)
-    free_device(torch)
+    cold = None
+    if not args.no_cold:
+        progress(f"{n}: cold launches")
+        cold = cold_pair(torch, w)
+        free_device(torch)
     extra = {}
     others = [] if args.no_extras else [c for c in workloads.CONFIG_NAMES if c != n]
     if args.no_decode and "decode" in others:
@@ -913,9 +917,10 @@ def main():
         progress(f"{name}: fused step")
         wc, entry = config_measure(torch, name, args, graph)
         free_device(torch)
-        progress(f"{name}: cold launches")
-        entry["cold_protocol"] = cold_pair(torch, wc)
-        free_device(torch)
+        if not args.no_cold:
+            progress(f"{name}: cold launches")
+            entry["cold_protocol"] = cold_pair(torch, wc)
+            free_device(torch)
         if name in big:
             progress(f"{name}: MXFP8 cache rows")
             _, mx = config_measure(torch, name, args, graph, cache="mxfp8")
@@ -1011,7 +1016,7 @@ def main():
                          "kernel_over_copy": main_m["achieved_GBps"] / ceil["GBps"],
                          "forms": ceil["forms"]},
         **({"pattern_ceiling": pattern} if pattern else {}),
-        "cold_protocol": cold,
+        **({"cold_protocol": cold} if cold else {}),
         **extra,
     }
     if not args.no_cpu_baseline:
