@@ -52,9 +52,9 @@ KERNEL_SRC = [os.path.join(ROOT, "causal_short_convolution_amd", "csrc", f)
               for f in ("kernels.hip", "device_common.h")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_kernels_traffic.md")
 COPY_BYTES = 512 << 20          # calibration copy: 512 MiB read + 512 MiB written
-KERNELS = ("prefill_kernel", "prefill_slice_kernel", "decode_kernel", "verify_kernel",
-           "commit_kernel", "mx_quantize_kernel", "backward_kernel", "backward_chunk_kernel",
-           "backward_final_kernel")
+KERNELS = ("prefill_kernel", "prefill_slice_kernel", "prefill_run_kernel", "decode_kernel",
+           "verify_kernel", "commit_kernel", "mx_quantize_kernel", "backward_kernel",
+           "backward_chunk_kernel", "backward_final_kernel")
 # DRAM-side request sizes on gfx950, as the calibration copy shows (512 MiB read in 4 Mi
 # TCC_EA0_RDREQ_DRAM requests, 512 MiB written in 8 Mi TCC_EA0_WRREQ_DRAM requests)
 DRAM_RD_BYTES, DRAM_WR_BYTES = 128, 64

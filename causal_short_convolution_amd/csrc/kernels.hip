@@ -772,6 +772,158 @@ __global__ void __launch_bounds__(kSliceBlock, (slice_min_waves<W, MX>()))
 }
 
 // ------------------------------------------------------------------------------------------------
+// Prefill over one-tensor slices, one run of RUN consecutive tokens of one 64-lane column slice
+// per wave (no LDS, no workgroup barrier). The run is walked in sub-spans of ST tokens: the rows of
+// sub-span n + 1 are loaded before sub-span n is computed, so a wave keeps loads in flight while
+// it computes, at about the registers of one 8-token span. The window is carried in registers
+// from one sub-span to the next; only the run's first R halo rows are loaded (from the previous
+// run, the stored state, or zeros). Tiles, sequence search, state rule, stores and row math are
+// those of prefill_slice_kernel, with a tile of RUN tokens per slice.
+// ------------------------------------------------------------------------------------------------
+#ifndef SC_RUN_TOKENS
+#define SC_RUN_TOKENS 16  // tokens per run
+#endif
+#ifndef SC_RUN_ST
+#define SC_RUN_ST 4
+#endif
+#ifndef SC_RUN_MIN_WAVES
+#define SC_RUN_MIN_WAVES 4
+#endif
+constexpr int kRunWaves = 4;  // waves per workgroup (independent)
+
+template <class E, int D, int W, int RUN, int ST, bool MX>
+__global__ void __launch_bounds__(64 * kRunWaves, SC_RUN_MIN_WAVES) prefill_run_kernel(StepArgs a) {
+    constexpr int VEC = E::VEC;
+    constexpr int LPH = D / VEC;
+    constexpr int R = W - 1;
+    constexpr int NS = RUN / ST;
+    static_assert(RUN % ST == 0 && RUN <= 64 && ST >= 1 && RUN >= R, "run");
+    using Rows = typename RowsFor<E, MX>::type;
+
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wl = threadIdx.x & 63;
+    const int slices = a.lane_blocks;
+    const int64_t units = (int64_t)a.tiles * slices;
+    const int64_t u = (int64_t)blockIdx.x * kRunWaves + w;
+    if (u >= units) return;  // the whole wave
+    const int slice = uniform((int32_t)(u % slices));
+    const int64_t tile = u / slices;
+    const int tensor = uniform(slice * 64 >= a.lanes_per_tensor ? 1 : 0);
+    const int c = slice * 64 + wl - tensor * a.lanes_per_tensor;
+    const int h = c / LPH;
+    const int d0 = (c - h * LPH) * VEC;
+    const int64_t T = a.tokens;
+    const char* x = static_cast<const char*>(tensor ? a.x[1] : a.x[0]);
+    const int64_t stride_bytes = (tensor ? a.x_stride[1] : a.x_stride[0]) * E::BYTES;
+    char* state = static_cast<char*>(tensor ? a.state[1] : a.state[0]);
+    const float* taps = tensor ? a.taps[1] : a.taps[0];
+    const int64_t row_bytes = (int64_t)a.heads * D * E::BYTES;
+    const uint32_t lane_off = (uint32_t)(((int64_t)h * D + d0) * E::BYTES);
+    char* stand_in = reinterpret_cast<char*>(const_cast<float*>(taps));  // >= one row long
+    const Rows rows = [&] {
+        if constexpr (MX)
+            return Rows(static_cast<char*>(tensor ? a.cache[1] : a.cache[0]),
+                        static_cast<char*>(tensor ? a.scales[1] : a.scales[0]),
+                        (uint32_t)(a.heads * D), h, d0, D, a.num_slots);
+        else
+            return Rows(static_cast<char*>(tensor ? a.cache[1] : a.cache[0]), (uint32_t)row_bytes,
+                        lane_off, a.num_slots);
+    }();
+
+    const int s = find_tile_seq<RUN>(a.cu, a.num_seqs, T, tile);
+    const int64_t start = uniform((int64_t)clamp_tok(a.cu[s], T));
+    int64_t end = uniform((int64_t)clamp_tok(a.cu[s + 1], T));
+    if (end < start) end = start;
+    const int64_t L = end - start;
+    const int64_t j = tile - tile_base<RUN>(a.cu, s, T);
+    const int64_t ntiles = L > 0 ? (L + RUN - 1) / RUN : 1;
+    if (j < 0 || j >= ntiles) return;  // the whole wave
+
+    const int64_t t0 = start + j * RUN;
+    const int64_t rem = end - t0;
+    const int n = rem <= 0 ? 0 : (rem < RUN ? (int)rem : RUN);
+    int32_t idx = -1;
+    bool slot_ok = false, read_state = false;
+    if (j == 0) {
+        idx = uniform(a.state_idx ? a.state_idx[s] : s);
+        slot_ok = R > 0 && state != nullptr && idx >= 0 && idx < a.num_state_slots;
+        read_state = slot_ok && (a.has_init ? a.has_init[s] != 0 : true);
+    }
+
+    // Loads in the order of use, all unconditional: the run's slots (lane i: token i's; a run
+    // with no rows reads a stand-in word), the halo (the R rows before the run, the stored state
+    // for a sequence's first run, else R stand-in rows, discarded), the first sub-span's rows
+    // (past the run's end the last row again; with no rows, the stand-in).
+    const int last = n > 0 ? n - 1 : 0;
+    const int64_t* sp = n > 0 ? a.slot + t0 + (wl < last ? wl : last)
+                              : reinterpret_cast<const int64_t*>(taps);
+    const int64_t slot_word = *sp;
+    const int64_t lane_slot = wl < n ? slot_word : (int64_t)-1;  // -1: the store is dropped
+    const char* hsrc = j > 0 ? x + (t0 - R) * stride_bytes
+                       : read_state ? state + (int64_t)idx * R * row_bytes
+                                    : stand_in;
+    const int64_t hstride = j > 0 ? stride_bytes : row_bytes;
+    uint4 halo[R > 0 ? R : 1];
+#pragma unroll
+    for (int k = 0; k < R; ++k) halo[k] = ldrow_keep(hsrc + k * hstride, lane_off);
+    const char* xb = n > 0 ? x + t0 * stride_bytes : stand_in;
+    const int64_t rstride = n > 0 ? stride_bytes : 0;
+    // the run's last R rows are the next run's halo: loaded without the streaming hint
+    const auto load_row = [&](int i) -> uint4 {
+        const char* p = xb + (i < last ? i : last) * rstride;
+        return i >= RUN - R ? ldrow_keep(p, lane_off) : ldrow(p, lane_off);
+    };
+    uint4 buf[2][ST];
+#pragma unroll
+    for (int i = 0; i < ST; ++i) buf[0][i] = load_row(i);
+
+    LaneParams<E, W> p;
+    load_params<E, W>(taps, tensor ? a.gamma[1] : a.gamma[0], a.heads, D, h, d0, p);
+    const float inv_d = 1.0f / (float)D;
+    if (j == 0 && !read_state) {
+#pragma unroll
+        for (int k = 0; k < R; ++k) halo[k] = make_uint4(0, 0, 0, 0);
+    }
+    float win[W][VEC];
+#pragma unroll
+    for (int k = 0; k < R; ++k) E::widen(halo[k], win[k]);
+
+#pragma unroll
+    for (int sub = 0; sub < NS; ++sub) {
+        if (sub + 1 < NS) {
+#pragma unroll
+            for (int i = 0; i < ST; ++i) buf[(sub + 1) & 1][i] = load_row((sub + 1) * ST + i);
+        }
+        // token tk's row goes to win[(tk + R) % W]; tokens past the run's end recompute the last
+        // row and their stores are dropped
+#pragma unroll
+        for (int i = 0; i < ST; ++i) {
+            const int tk = sub * ST + i;
+            E::widen(buf[sub & 1][i], win[(tk + R) % W]);
+            float o[VEC];
+            fused_row<E, W, LPH>(win, tk % W, p, a.eps, inv_d, o);
+            rows.write(lane_value(lane_slot, tk), rows.encode(o));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // The sequence's first run writes its new state (it read the old one), as in prefill_kernel.
+    if (R > 0 && j == 0 && slot_ok) {
+        char* dst = state + (int64_t)idx * R * row_bytes;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int64_t e = L + i;
+            uint4 r = make_uint4(0, 0, 0, 0);
+            if (e >= R)
+                r = ldrow(x + (start + e - R) * stride_bytes, lane_off);
+            else if (read_state)
+                r = ldrow(dst + e * row_bytes, lane_off);
+            if (e != i || !read_state) strow(dst + i * row_bytes, lane_off, r);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
 // Decode: one token per sequence; window = [state rows 0..W-2, new row]; state shifts by one.
 // ------------------------------------------------------------------------------------------------
 template <class E, int D, int W, bool MX>
@@ -1025,6 +1177,13 @@ constexpr KernelFn prefill_slice_mx_fn() {
         return prefill_slice_kernel<E, D, W, slice_span_tokens<W, true>(), true>;
     else return prefill_kernel<E, D, W, span_tokens<W, true>(), true, true>;
 }
+// MXFP8 rows over one-tensor slices in runs (large problems, see use_run_kernel)
+template <class E, int D, int W>
+constexpr KernelFn prefill_run_mx_fn() {
+    if constexpr (W <= SC_SLICE_MAX_W)
+        return prefill_run_kernel<E, D, W, SC_RUN_TOKENS, SC_RUN_ST, true>;
+    else return nullptr;
+}
 template <class E, int D, int W>
 constexpr KernelFn decode_fn() { return decode_kernel<E, D, W, false>; }
 template <class E, int D, int W>
@@ -1049,6 +1208,7 @@ const KernelFn kDecode[2][3][8] = SC_TABLE(decode);
 const KernelFn kPrefillMx[2][3][8] = SC_TABLE(prefill_mx);
 const KernelFn kPrefillSlice[2][3][8] = SC_TABLE(prefill_slice);
 const KernelFn kPrefillSliceMx[2][3][8] = SC_TABLE(prefill_slice_mx);
+const KernelFn kPrefillRunMx[2][3][8] = SC_TABLE(prefill_run_mx);
 const KernelFn kDecodeMx[2][3][8] = SC_TABLE(decode_mx);
 const KernelFn kQuantizeMx[2][3] = {
     {mx_quantize_kernel<F32, 64>, mx_quantize_kernel<F32, 128>, mx_quantize_kernel<F32, 256>},
@@ -1071,6 +1231,23 @@ bool use_slice_kernel(int width, int64_t lanes_per_tensor) {
     return width <= SC_SLICE_MAX_W && lanes_per_tensor % 64 == 0;
 }
 
+// MXFP8 rows in runs (prefill_run_kernel) when the grid has at least SC_RUN_MIN_GRID_WAVES waves
+// (8 rounds of the 4 096 wave slots MI355X has at 4 waves per SIMD): there its overlap of each
+// wave's arithmetic with its next loads pays; on smaller grids the last partial round and the
+// longer-lived waves cost more. Measured on MI355X (MXFP8 rows, one process, runs of 16 / 32
+// tokens against prefill_slice_kernel): 64 chunks of 2 048 resumed tokens, 16 KV heads x 128
+// (65 536 waves) 313.6 / 313.4 against 351.3 us; 17 060 packed tokens, 8 KV heads x 128
+// (4 265 / 2 132 waves) 26.4 / 29.0 against 24.8 us. bf16 rows were slower in runs at both sizes
+// (mixed 398.0 / 417.0 against 368.0 us).
+#ifndef SC_RUN_MIN_GRID_WAVES
+#define SC_RUN_MIN_GRID_WAVES 32768
+#endif
+bool use_run_kernel(int width, bool mx, int64_t lanes_per_tensor, int64_t tokens) {
+    if (!mx || !use_slice_kernel(width, lanes_per_tensor)) return false;
+    const int64_t slices = 2 * lanes_per_tensor / 64;
+    return tokens / SC_RUN_TOKENS * slices >= SC_RUN_MIN_GRID_WAVES;
+}
+
 int compute_units() {
     static int cached[64];
     int dev = 0;
@@ -1087,7 +1264,8 @@ int compute_units() {
 
 }  // namespace
 
-int prefill_tile_tokens(int width, bool mx, int64_t lanes_per_tensor) {
+int prefill_tile_tokens(int width, bool mx, int64_t lanes_per_tensor, int64_t tokens) {
+    if (use_run_kernel(width, mx, lanes_per_tensor, tokens)) return SC_RUN_TOKENS;
     if (use_slice_kernel(width, lanes_per_tensor)) {
         const int bt = width <= 4 ? (mx ? slice_span_tokens<1, true>() : slice_span_tokens<1, false>())
                                   : (mx ? slice_span_tokens<8, true>() : slice_span_tokens<8, false>());
@@ -1105,6 +1283,12 @@ hipError_t launch_prefill(StepArgs a, int dtype, int head_dim, int width, bool m
     // a grid sized to the chip (a multiple of the slice count) walks the units.
     a.lane_blocks = (int32_t)((2 * (int64_t)a.lanes_per_tensor + 63) / 64);
     const int64_t units = (int64_t)a.tiles * a.lane_blocks;
+    if (use_run_kernel(width, mx, a.lanes_per_tensor, a.tokens)) {  // one unit per wave
+        hipLaunchKernelGGL(kPrefillRunMx[dtype][d_index(head_dim)][width - 1],
+                           dim3((unsigned)((units + kRunWaves - 1) / kRunWaves)),
+                           dim3(64 * kRunWaves), 0, stream, a);
+        return hipGetLastError();
+    }
     if (use_slice_kernel(width, a.lanes_per_tensor)) {
         int64_t grid = units;
         if (SC_SLICE_WG_PER_CU > 0) {

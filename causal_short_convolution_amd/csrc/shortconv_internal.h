@@ -95,7 +95,8 @@ hipError_t launch_verify(StepArgs a, VerifyArgs va, int dtype, int head_dim, int
 hipError_t launch_commit(StepArgs a, VerifyArgs va, int dtype, int head_dim, int width,
                          hipStream_t stream);
 
-// Tokens per prefill tile (4 spans) for a width, cache format and row width in lanes.
-int prefill_tile_tokens(int width, bool mx, int64_t lanes_per_tensor);
+// Tokens per prefill tile for a width, cache format, row width in lanes and token count (the
+// kernel, and so the tile, depends on all four).
+int prefill_tile_tokens(int width, bool mx, int64_t lanes_per_tensor, int64_t tokens);
 
 }  // namespace sc

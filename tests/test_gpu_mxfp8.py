@@ -336,3 +336,72 @@ def test_varlen_workload_mx_rows_at_full_size():
             assert (tie | ~((gc != ec) & same)).all(), "a code differs off an E4M3 midpoint"
     for a, b in ((plain.k_state, mx.k_state), (plain.v_state, mx.v_state)):
         assert np.array_equal(to_host(a, "bf16"), to_host(b, "bf16"))
+
+
+def _check_mx_against_plain_bf16(w, plain, mx, every=4096):
+    """MXFP8 bytes of a bf16 workload against the oracle's quantization of the plain kernel's
+    bf16 rows: equal except at double-rounding ties (an E4M3 midpoint, a power-of-two block
+    maximum). Checked on the blocks of 4 096 written rows that start every `every` rows (every
+    row by default); the conv state in full."""
+    rows = _written_slots(w)
+    mids = oracle.e4m3_decode(np.arange(0, 0x7E))
+    mids = (mids + oracle.e4m3_decode(np.arange(1, 0x7F))) / 2.0
+    for cache, codes_d, scales_d in ((plain.k_cache, mx.k_codes, mx.k_scales),
+                                     (plain.v_cache, mx.v_codes, mx.v_scales)):
+        for a in range(0, rows.size, every):
+            sel = rows[a:a + 4096]
+            idx = torch.from_numpy(sel).to(DEV)
+            yb = oracle.widen(to_host(cache.index_select(0, idx), "bf16"))
+            ec, es = oracle.mxfp8_quantize(yb)
+            gc = codes_d.index_select(0, idx).cpu().numpy()
+            gs = scales_d.index_select(0, idx).cpu().numpy()
+            blocks = np.abs(yb).reshape(*yb.shape[:-1], -1, 32).max(-1)
+            pow2 = (blocks > 0) & (np.frexp(blocks)[0] == 0.5)
+            assert (pow2 | (gs == es)).all(), "a scale differs off a power-of-two block maximum"
+            same = np.repeat(gs == es, 32, axis=-1)
+            e = np.repeat(es.astype(np.int64) - 127, 32, axis=-1)
+            tie = np.isin(np.abs(yb) * np.exp2(-e.astype(np.float64)), mids)
+            assert (tie | ~((gc != ec) & same)).all(), "a code differs off an E4M3 midpoint"
+    for a, b in ((plain.k_state, mx.k_state), (plain.v_state, mx.v_state)):
+        assert np.array_equal(to_host(a, "bf16"), to_host(b, "bf16"))
+
+
+def test_mixed_workload_mx_rows_at_full_size():
+    """The mixed workload (64 resumed chunks of 2 048 tokens, 16 KV heads x 128, then 512
+    decodes) with MXFP8 rows at full size. Its prefill grid is large enough (131 072 tokens / 16
+    x 8 column slices = 65 536 waves) for the library to run MXFP8 rows in 16-token runs per
+    wave, so this checks that kernel against the plain kernel's rows and the oracle quantizer (on
+    a quarter of the rows: a block of 4 096 in every 16 384, spread over the whole step)."""
+    w = workloads.config("mixed")
+    plain, mx = _fused_pair(w)
+    _check_mx_against_plain_bf16(w, plain, mx, every=16384)
+
+
+@pytest.mark.parametrize("W", [1, 3])
+def test_fused_mx_runs_equal_quantized_fp32_output(W):
+    """fp32 I/O, 16 KV heads x 256: 32 column slices, so 17 000 packed tokens (ragged sequences,
+    some resuming from a stored state, a few dropped slots) make a grid of 33 984 waves, enough
+    for the 16-token runs per wave. Codes and scales are the oracle quantizer's on the plain
+    kernel's fp32 rows, bit for bit; the conv state is the plain run's."""
+    spec = workloads.Spec(dtype="f32", H=16, D=256, W=W, seed=90 + W,
+                          prefill_lens=[5000, 1, 17, 0, 3333, 6000, 2649],
+                          has_init=[1, 0, 1, 1, 0, 1, 0], pad_slot_every=977, outlier_p=0.01)
+    w = workloads.build(spec)
+    assert sum(spec.prefill_lens) // 16 * 32 >= 32768
+    plain, mx = _fused_pair(w)
+    rows = _written_slots(w)
+    for cache, codes, scales in ((plain.k_cache, mx.k_codes, mx.k_scales),
+                                 (plain.v_cache, mx.v_codes, mx.v_scales)):
+        for a in range(0, rows.size, 2048):
+            sel = rows[a:a + 2048]
+            idx = torch.from_numpy(sel).to(DEV)
+            y32 = to_host(cache.index_select(0, idx), "f32").astype(np.float64)
+            ec, es = oracle.mxfp8_quantize(y32)
+            assert np.array_equal(scales.index_select(0, idx).cpu().numpy(), es)
+            assert np.array_equal(codes.index_select(0, idx).cpu().numpy(), ec)
+        untouched = np.setdiff1d(np.arange(w.num_slots), rows)
+        assert (codes.cpu().numpy()[untouched] == 0xA5).all()
+        assert (scales.cpu().numpy()[untouched] == 0xA5).all()
+    for a, b in ((plain.k_state, mx.k_state), (plain.v_state, mx.v_state)):
+        if a is not None:  # (W = 1 keeps no state)
+            assert np.array_equal(to_host(a, "f32"), to_host(b, "f32")), "state must not change"
