@@ -405,3 +405,17 @@ def test_fused_mx_runs_equal_quantized_fp32_output(W):
     for a, b in ((plain.k_state, mx.k_state), (plain.v_state, mx.v_state)):
         if a is not None:  # (W = 1 keeps no state)
             assert np.array_equal(to_host(a, "f32"), to_host(b, "f32")), "state must not change"
+
+
+def test_fused_mx_runs_bf16_narrow_heads():
+    """bf16 rows, 32 KV heads x 64 (8 lanes per head), W = 2: 8 column slices, so 70 000 packed
+    tokens make a grid of 35 000 waves and the library runs MXFP8 rows in 16-token runs. Bytes
+    against the oracle quantizer of the plain kernel's rows (double-rounding ties aside), on a
+    quarter of the rows; the conv state in full."""
+    spec = workloads.Spec(dtype="bf16", H=32, D=64, W=2, seed=77,
+                          prefill_lens=[30000, 7, 0, 19993, 20000], has_init=[1, 0, 1, 0, 1],
+                          pad_slot_every=1009, outlier_p=0.01)
+    w = workloads.build(spec)
+    assert sum(spec.prefill_lens) // 16 * 8 >= 32768
+    plain, mx = _fused_pair(w)
+    _check_mx_against_plain_bf16(w, plain, mx, every=16384)
