@@ -24,7 +24,12 @@
 // sequence s owns tiles [P(s), P(s) + max(1, ceil(L_s / (4*BT)))) with P(s) = floor(cu[s] /
 // (4*BT)) + s. P is strictly increasing and P(s) + max(1, ceil(L_s/(4*BT))) <= P(s+1), so a
 // workgroup finds its sequence by a wave-parallel search over cu_seqlens (one vector load per 64x
-// narrowing) with no host-side scan; at most one tile per sequence is empty.
+// narrowing, whose lanes also hold the sequence's bounds when there are at most 63 sequences)
+// with no host-side scan; at most one tile per sequence is empty.
+//
+// MXFP8 rows over one-tensor slices on large grids instead take one run of 16 tokens per wave
+// (prefill_run_kernel): the run's rows are loaded one 4-token sub-span ahead of the arithmetic
+// and the window is carried in registers, which hides the encoder's extra arithmetic.
 //
 // Memory order within a wave: after the search, every load of the span goes out back to back
 // (parameters, halo, the rows the next wave needs first, the other rows, the span's slots as one
@@ -670,12 +675,11 @@ __global__ void __launch_bounds__(kSliceBlock, (slice_min_waves<W, MX>()))
 
     for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
         const int64_t tile = u / slices;
-        const int s = find_tile_seq<BB>(a.cu, a.num_seqs, T, tile);
-        const int64_t start = uniform((int64_t)clamp_tok(a.cu[s], T));
-        int64_t end = uniform((int64_t)clamp_tok(a.cu[s + 1], T));
+        int64_t start, end;
+        const int s = tile_seq_bounds<BB>(a.cu, a.num_seqs, T, tile, start, end);
         if (end < start) end = start;
         const int64_t L = end - start;
-        const int64_t j = tile - tile_base<BB>(a.cu, s, T);
+        const int64_t j = tile - (start / BB + s);
         const int64_t ntiles = L > 0 ? (L + BB - 1) / BB : 1;
         if (j < 0 || j >= ntiles) continue;  // the same for the whole workgroup
 
@@ -830,12 +834,11 @@ __global__ void __launch_bounds__(64 * kRunWaves, SC_RUN_MIN_WAVES) prefill_run_
                         lane_off, a.num_slots);
     }();
 
-    const int s = find_tile_seq<RUN>(a.cu, a.num_seqs, T, tile);
-    const int64_t start = uniform((int64_t)clamp_tok(a.cu[s], T));
-    int64_t end = uniform((int64_t)clamp_tok(a.cu[s + 1], T));
+    int64_t start, end;
+    const int s = tile_seq_bounds<RUN>(a.cu, a.num_seqs, T, tile, start, end);
     if (end < start) end = start;
     const int64_t L = end - start;
-    const int64_t j = tile - tile_base<RUN>(a.cu, s, T);
+    const int64_t j = tile - (start / RUN + s);
     const int64_t ntiles = L > 0 ? (L + RUN - 1) / RUN : 1;
     if (j < 0 || j >= ntiles) return;  // the whole wave
 
