@@ -1235,15 +1235,16 @@ bool use_slice_kernel(int width, int64_t lanes_per_tensor) {
 }
 
 // MXFP8 rows in runs (prefill_run_kernel) when the grid has at least SC_RUN_MIN_GRID_WAVES waves
-// (8 rounds of the 4 096 wave slots MI355X has at 4 waves per SIMD): there its overlap of each
+// (4 rounds of the 4 096 wave slots MI355X has at 4 waves per SIMD): there its overlap of each
 // wave's arithmetic with its next loads pays; on smaller grids the last partial round and the
-// longer-lived waves cost more. Measured on MI355X (MXFP8 rows, one process, runs of 16 / 32
-// tokens against prefill_slice_kernel): 64 chunks of 2 048 resumed tokens, 16 KV heads x 128
-// (65 536 waves) 313.6 / 313.4 against 351.3 us; 17 060 packed tokens, 8 KV heads x 128
-// (4 265 / 2 132 waves) 26.4 / 29.0 against 24.8 us. bf16 rows were slower in runs at both sizes
-// (mixed 398.0 / 417.0 against 368.0 us).
+// longer-lived waves cost more. Measured on MI355X (MXFP8 rows, bf16 inputs, 8 or 16 KV heads x
+// 128, one process; runs of 16 tokens against prefill_slice_kernel): 64 chunks of 2 048 resumed
+// tokens, 16 heads (65 536 waves) 313.6 against 351.3 us; 16 sequences of 4 096 tokens (16 384
+// waves) 80.3 against 86.1 us; 16 of 2 048 (8 192 waves) 41.9 against 41.2 us; 17 060 packed
+// tokens (4 265 waves) 26.4 against 24.8 us. bf16 rows were slower in runs at every size
+// measured (65 536 waves: 398.0 against 368.0 us).
 #ifndef SC_RUN_MIN_GRID_WAVES
-#define SC_RUN_MIN_GRID_WAVES 32768
+#define SC_RUN_MIN_GRID_WAVES 16384
 #endif
 bool use_run_kernel(int width, bool mx, int64_t lanes_per_tensor, int64_t tokens) {
     if (!mx || !use_slice_kernel(width, lanes_per_tensor)) return false;
